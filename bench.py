@@ -1,0 +1,231 @@
+"""Benchmark of one data-parallel rank's shard-local mixed-precision AdamW step.
+
+A step is one pass of the whole hot path over one batch of synthetic
+gradients already resident in HBM:
+  host plan (zero_partition, zero_bucket_plan)
+  -> zero_bucket_flatten: per-tensor 16-bit grads into the flat grad shard,
+     one call per constant-size fused buffer (500M elements)
+  -> zero_grad_stats: overflow flag + squared norm (fp64)
+  -> zero_adam_step: fused AdamW on fp32 master/m/v, writes 16-bit params
+Workload: GPT-2-1.5B-like parameter list (48 layers, hidden 1600, vocab
+50257, fp16) at Nd=1, so the rank's shard is all 1,557,611,200 parameters;
+loss scale 2^16, clip 1.0.
+
+Prints one JSON line.  `value` is parameters per second of the whole step;
+the roofline object covers the fused AdamW kernel (28 algorithmic bytes per
+parameter: read grad 2 + master/m/v 12, write master/m/v 12 + param 2).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E
+ADAM_BYTES_PER_PARAM = 28
+STATS_BYTES_PER_PARAM = 2
+FLATTEN_BYTES_PER_PARAM = 4  # 16-bit read + write
+METRIC = "Adam-shard params/sec + achieved HBM GB/s vs peak (28 B/param)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "adamw_stream_gpt2-1.5b_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "zero_sharded_mixed_grads_amd", "csrc", "zero_kernels.hip")
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Workload:
+    def __init__(self, cfg_idx: int, device):
+        import torch
+        import zero_sharded_mixed_grads_amd as z
+        from synth import CONFIGS, gen
+
+        self.z, self.torch = z, torch
+        cfg = self.cfg = CONFIGS[cfg_idx]
+        self.dev = device
+        self.begin, self.end = z.zero_partition(cfg.psi, cfg.nd, cfg.rank)
+        n = self.n = self.end - self.begin
+        tdt = gen.torch_dtype(cfg.dtype)
+        log(f"[bench] workload {cfg.name}: psi={cfg.psi} nd={cfg.nd} rank={cfg.rank} n={n}")
+        t0 = time.time()
+        # per-tensor gradients as backward would leave them (only those in the shard)
+        plan = z.zero_bucket_plan(cfg.numels, cfg.psi, self.begin, self.end)
+        self.tensor_ids = sorted({s[1] for s in plan})
+        self.grads = [None] * len(cfg.numels)
+        for i in self.tensor_ids:
+            t = torch.empty(cfg.numels[i], dtype=tdt, device=device)
+            gen.device_fill_normal_(t, cfg.grad_seed(0) * 100003 + i, cfg.grad_sigma,
+                                    cfg.loss_scale)
+            self.grads[i] = t
+        self.g = torch.empty(n, dtype=tdt, device=device)          # flat grad shard
+        self.master = torch.empty(n, dtype=torch.float32, device=device)
+        gen.device_fill_normal_(self.master, cfg.master_seed(), cfg.master_sigma)
+        self.m = torch.zeros(n, dtype=torch.float32, device=device)
+        self.v = torch.zeros(n, dtype=torch.float32, device=device)
+        self.p = torch.empty(n, dtype=tdt, device=device)
+        self.stats = z.new_grad_stats(device)
+        self.state = z.new_adam_state(device)
+        self.ws = z.new_workspace(n, device)
+        self.hp = z.adamw(**cfg.hp.__dict__)
+        self.ptrs = [t.data_ptr() if t is not None else None for t in self.grads]
+        torch.cuda.synchronize()
+        log(f"[bench] inputs resident in HBM after {time.time() - t0:.1f}s "
+            f"({torch.cuda.memory_allocated() / 1e9:.1f} GB allocated)")
+
+    def step(self, ev=None):
+        """One pass of the hot path; ev: optional list of 4 events recorded
+        around flatten / stats / adam on the launch stream."""
+        z, cfg = self.z, self.cfg
+        stream = self.torch.cuda.current_stream()
+        s = stream.cuda_stream
+        b, e = z.zero_partition(cfg.psi, cfg.nd, cfg.rank)
+        B = cfg.bucket_elems or cfg.psi
+        if ev: ev[0].record(stream)
+        lo = b
+        while lo < e:  # one fused buffer at a time, this rank's part of it
+            hi = min((lo // B + 1) * B, e)
+            z.zero_bucket_flatten(self.ptrs, cfg.numels, cfg.dtype, lo, hi - lo,
+                                  self.g.data_ptr() + 2 * (lo - b), s)
+            lo = hi
+        if ev: ev[1].record(stream)
+        z.zero_grad_stats(self.g, cfg.dtype, self.n, cfg.hp.inv_loss_scale, self.ws,
+                          self.ws.numel(), self.stats, s)
+        if ev: ev[2].record(stream)
+        z.zero_adam_step(self.hp, self.g, cfg.dtype, self.master, self.m, self.v, self.p,
+                         cfg.dtype, self.n, self.stats, self.state, s)
+        if ev: ev[3].record(stream)
+
+
+def cpu_baseline(w, target_s: float = 12.0):
+    """The oracle, as it is, on a bounded contiguous sample of the same shard
+    (copied to host memory): grad stats + AdamW on the sample."""
+    import oracle
+    from synth import AdamW
+    torch = w.torch
+    cfg = w.cfg
+
+    def host(t, lo, k, np_dt):
+        return t[lo:lo + k].cpu().numpy().view(np_dt).copy()
+
+    def run(k):
+        gb = host(w.g, 0, k, np.uint16)
+        th, m, v = (host(a, 0, k, np.float32) for a in (w.master, w.m, w.v))
+        p = np.zeros(k, np.uint16)
+        t0 = time.perf_counter()
+        sq, ov = oracle.grad_stats(gb, cfg.dtype, cfg.hp.inv_loss_scale)
+        s = oracle.step_scalars(cfg.hp, True, sq, ov, 0)
+        oracle.adamw_(s, gb, cfg.dtype, th, m, v, p, cfg.dtype)
+        return time.perf_counter() - t0
+
+    k = min(w.n, 1 << 22)
+    dt = run(k)
+    k2 = int(min(w.n, max(k, k * target_s / max(dt, 1e-6))))
+    dt2 = run(k2) if k2 > k else dt
+    k_used = k2 if k2 > k else k
+    return {"value": k_used / dt2, "unit": "params/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"first {k_used} elements of the same shard in host memory, "
+                      f"fp64 grad stats + AdamW ({dt2:.1f} s)"}
+
+
+def load_traffic(n_params: int):
+    """HBM bytes per Adam launch from the committed rocprofv3 counter runs,
+    or None if the kernel source changed since they were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    d = json.load(open(TRAFFIC_FILE))
+    if d.get("kernel_source_sha256_16") != kernel_source_hash() or d.get("n") != n_params:
+        return None
+    return d.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one data-parallel rank's shard on one GPU; runs on more "
+              "than one GPU are not supported by this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = Workload(args.config, dev)
+
+    for _ in range(args.warmup):
+        w.step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        w.step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([[a.elapsed_time(b) for a, b in zip(e[:-1], e[1:])] for e in evs])
+    flat_ms, stats_ms, adam_ms = ms.mean(axis=0)
+    log(f"[bench] timed {args.steps} steps in {wall:.3f}s; per step flatten {flat_ms:.3f} ms, "
+        f"stats {stats_ms:.3f} ms, adam {adam_ms:.3f} ms")
+
+    n = w.n
+    step_ms = wall * 1e3 / args.steps
+    adam_gbs = ADAM_BYTES_PER_PARAM * n / (adam_ms * 1e-3) / 1e9
+    traffic = load_traffic(n)
+    out = {
+        "metric": METRIC,
+        "value": n / (step_ms * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.cfg.name + f"-nd{w.cfg.nd}-rank{w.cfg.rank}", "psi": w.cfg.psi,
+                   "nd": w.cfg.nd, "rank": w.cfg.rank, "shard_params": n,
+                   "grad_dtype": w.cfg.dtype, "param_dtype": w.cfg.dtype,
+                   "bucket_elems": w.cfg.bucket_elems, "max_grad_norm": w.cfg.hp.max_grad_norm,
+                   "loss_scale": w.cfg.loss_scale},
+        "roofline": {"bound": "hbm", "achieved": adam_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": adam_gbs / HBM_PEAK_GBS, "traffic": traffic},
+        "kernels": {
+            "adam_step": {"ms": adam_ms, "params_per_s": n / (adam_ms * 1e-3),
+                          "GB/s": adam_gbs, "bytes_per_param": ADAM_BYTES_PER_PARAM},
+            "grad_stats": {"ms": stats_ms,
+                           "GB/s": STATS_BYTES_PER_PARAM * n / (stats_ms * 1e-3) / 1e9,
+                           "bytes_per_param": STATS_BYTES_PER_PARAM},
+            "bucket_flatten": {"ms": flat_ms,
+                               "GB/s": FLATTEN_BYTES_PER_PARAM * n / (flat_ms * 1e-3) / 1e9,
+                               "bytes_per_param": FLATTEN_BYTES_PER_PARAM},
+        },
+        "step_bytes_per_param": ADAM_BYTES_PER_PARAM + STATS_BYTES_PER_PARAM +
+                                FLATTEN_BYTES_PER_PARAM,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

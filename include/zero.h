@@ -1,0 +1,214 @@
+/*
+ * zero.h - C ABI of libzero_mi355x: one data-parallel rank's shard-local
+ * mixed-precision AdamW step of ZeRO-DP (P_os / P_os+g), for AMD MI355X
+ * (gfx950).
+ *
+ * Sources (web pages on ZeRO):
+ *  [P2] "ZeRO: Memory Optimizations Toward Training Trillion Parameter Models"
+ *       (paper summary page): section 問題設定 > メモリ消費の定量化 (the five
+ *       model-state arrays of mixed-precision Adam, 16 bytes per parameter),
+ *       section 提案手法 > ZeRO-DP (Stage 1 P_os, Stage 2 P_os+g, Stage 3
+ *       P_os+g+p, and the memory table), section ZeRO-R > CB (constant-size
+ *       fused buffers), section 考察 (optimizer state is needed only at the
+ *       end of the step).
+ *  [P4] "ZeRO" (AI-library tutorial page): section 显存背景 (bf16/fp16 +
+ *       AdamW + fp32 master = 16 bytes per parameter) and sections
+ *       ZeRO-1 / ZeRO-2 / ZeRO-3 (per-stage memory equations).
+ *
+ * Conventions shared by every call:
+ *  - Every call returns a zero_status; ZERO_OK is 0.  Nothing is thrown
+ *    across the ABI.  After a failure, zero_last_error() returns a
+ *    thread-local, NUL-terminated description of it.
+ *  - The caller owns all memory.  The library never allocates device memory;
+ *    the workspace size of zero_grad_stats comes from a query call.
+ *  - Device calls are asynchronous and ordered on the caller's HIP stream,
+ *    passed as `void *stream` (a hipStream_t; NULL is the null stream).  They
+ *    never synchronise and never read device data on the host.  Argument
+ *    checks happen on the host before any launch; a launch failure reported
+ *    by the runtime returns ZERO_EDEVICE.
+ *  - Device pointers are plain device addresses (e.g. a torch tensor's
+ *    data_ptr()).  Counts and offsets are 64-bit element counts.
+ *  - 16-bit buffers need 2-byte alignment and fp32 buffers 4-byte alignment;
+ *    any other offset ("phase") inside a 16-byte line is legal and handled.
+ *  - Output buffers must not overlap input buffers (ZERO_EINVAL), except for
+ *    the documented in-place arrays.
+ */
+#ifndef ZERO_MI355X_H
+#define ZERO_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ZERO_OK = 0,
+    ZERO_EINVAL = 1, /* an argument is out of its domain */
+    ZERO_ENOSPC = 2, /* a caller-provided capacity (segments, workspace) is too small */
+    ZERO_EALIGN = 3, /* a pointer is not aligned to its element size */
+    ZERO_EDEVICE = 4 /* the HIP runtime reported an error for a launch */
+} zero_status;
+
+typedef enum { ZERO_F32 = 0, ZERO_F16 = 1, ZERO_BF16 = 2 } zero_dtype;
+
+/* Static name of a status code. */
+const char *zero_status_str(zero_status s);
+
+/* Thread-local detail of the last failing call made by this thread ("" if
+ * none).  The string stays valid until the next failing call on the thread. */
+const char *zero_last_error(void);
+
+/* ---------------------------------------------------------------- planner
+ * Host-only, pure functions: no device access. */
+
+/* [P2] ZeRO-DP, Stage 1: the flat vector of psi parameters is cut into nd
+ * parts and each data-parallel rank keeps and updates only its own part.
+ * Rank `rank` owns the contiguous range [*begin, *end).  When nd does not
+ * divide psi, the parts differ in size by at most one element and the first
+ * (psi mod nd) ranks hold the larger size; the ranges tile [0, psi) with no
+ * padding.  Errors: ZERO_EINVAL if nd == 0, rank >= nd or an output pointer
+ * is NULL. */
+zero_status zero_partition(uint64_t psi, uint32_t nd, uint32_t rank, uint64_t *begin,
+                           uint64_t *end);
+
+/* [P2] memory accounting and the ZeRO-DP table; [P4] ZeRO-1/2/3 equations.
+ * Model-state bytes held by the busiest rank: 2 bytes of 16-bit params,
+ * 2 bytes of 16-bit grads and k bytes of optimizer state per parameter
+ * (k = 12 for mixed-precision Adam: fp32 master, momentum, variance).
+ *   stage 0 (plain DP):  (4 + k) psi
+ *   stage 1 (P_os):      4 psi + k S
+ *   stage 2 (P_os+g):    2 psi + (2 + k) S
+ *   stage 3 (P_os+g+p):  (4 + k) S
+ * with S = ceil(psi / nd), the largest part.  Activations, communication
+ * buffers and allocator overhead are not model states and are not counted.
+ * Errors: ZERO_EINVAL if stage > 3, nd == 0, bytes is NULL or the result
+ * does not fit in 64 bits. */
+zero_status zero_mem_bytes(uint32_t stage, uint64_t psi, uint32_t nd, uint32_t k,
+                           uint64_t *bytes);
+
+/* One piece of the bucket layout: elements [src_off, src_off + len) of
+ * tensor `tensor` land at [dst_off, dst_off + len) of a buffer that holds
+ * the planned range; the piece lies inside bucket window `bucket`. */
+typedef struct {
+    uint64_t bucket, tensor, src_off, dst_off, len;
+} zero_segment;
+
+/* [P2] ZeRO-R, CB: gradients are gathered into fused buffers of a constant
+ * size instead of model-sized temporaries.  The n_tensors tensors (element
+ * counts numel[]) are laid end to end in list order, without padding, into a
+ * flat stream of psi = sum(numel) elements, and the stream is cut into
+ * windows of bucket_elems elements (bucket b = [b*bucket_elems,
+ * min((b+1)*bucket_elems, psi)); a tensor may straddle two windows).  The
+ * plan lists, in flat order, every non-empty intersection of a tensor with a
+ * window and with [range_begin, range_end); dst_off counts from range_begin.
+ * Writes at most `cap` segments to segs (segs may be NULL when cap == 0) and
+ * always stores the full count in *n_segs.  Errors: ZERO_EINVAL for
+ * bucket_elems == 0, range_begin > range_end, range_end > psi, a NULL numel
+ * with n_tensors > 0, or a NULL n_segs; ZERO_ENOSPC if cap < *n_segs (the
+ * first cap segments are still written). */
+zero_status zero_bucket_plan(const uint64_t *numel, uint32_t n_tensors, uint64_t bucket_elems,
+                             uint64_t range_begin, uint64_t range_end, zero_segment *segs,
+                             uint64_t cap, uint64_t *n_segs);
+
+/* ------------------------------------------------------------ device calls */
+
+/* [P2] ZeRO-R, CB and MD: copies elements [range_begin, range_begin + count)
+ * of the list-order flat stream of the tensors into the contiguous device
+ * buffer dst (count elements of type dt), bit for bit.  With bucket size B,
+ * bucket b is range_begin = b*B, count = min(B, psi - b*B); a rank's part of
+ * the stream is range_begin = begin, count = end - begin.
+ * tensor_ptrs (host array of n_tensors device pointers) and numel (host
+ * array) describe the tensors; a pointer may be NULL only for a tensor that
+ * does not intersect the range.  dst bytes beyond count are not written.
+ * Errors: ZERO_EINVAL (dt not F32/F16/BF16, range beyond the stream, NULL
+ * pointers, dst overlapping an intersecting source), ZERO_EALIGN (a pointer
+ * not aligned to the element size), ZERO_EDEVICE.  count == 0 is a no-op. */
+zero_status zero_bucket_flatten(const void *const *tensor_ptrs, const uint64_t *numel,
+                                uint32_t n_tensors, zero_dtype dt, uint64_t range_begin,
+                                uint64_t count, void *dst, void *stream);
+
+/* Device-resident result of zero_grad_stats (16 bytes, 8-byte aligned). */
+typedef struct {
+    double sq_norm;    /* sum over the shard of (g / loss_scale)^2 */
+    uint32_t overflow; /* 1 if any stored gradient is inf or NaN, else 0 */
+    uint32_t pad;
+} zero_grad_stats_t;
+
+/* Bytes of device workspace that zero_grad_stats needs for n gradients. */
+zero_status zero_grad_stats_workspace(uint64_t n, size_t *bytes);
+
+/* Mixed-precision gradient statistics of one rank's gradient shard ([P2]
+ * memory accounting: fp16 gradients of mixed-precision training; [P2]
+ * ZeRO-DP Stage 2: each rank holds only its part of the gradients).  Reads
+ * n 16-bit gradients (gdt F16 or BF16, stored multiplied by the loss
+ * scale), and writes *d_stats (device memory) with the overflow flag (any
+ * non-finite element) and the squared L2 norm of g * inv_loss_scale,
+ * accumulated in fp64 in a fixed order (bit-reproducible for a given n).
+ * sq_norm is unspecified when overflow is set.  n == 0 writes {0, 0}.
+ * Multi-rank callers sum sq_norm and take the max of overflow across ranks
+ * on the same stream before zero_adam_step.
+ * workspace: device memory of at least zero_grad_stats_workspace(n) bytes,
+ * 16-byte aligned; its contents are scratch.  Errors: ZERO_EINVAL (NULL
+ * grad with n > 0, NULL d_stats, bad dtype, inv_loss_scale not finite and
+ * positive), ZERO_ENOSPC (workspace too small), ZERO_EALIGN, ZERO_EDEVICE. */
+zero_status zero_grad_stats(const void *grad, zero_dtype gdt, uint64_t n, double inv_loss_scale,
+                            void *workspace, size_t ws_bytes, zero_grad_stats_t *d_stats,
+                            void *stream);
+
+/* AdamW hyper-parameters (host memory, fp64). */
+typedef struct {
+    double lr, beta1, beta2, eps, weight_decay;
+    double max_grad_norm;  /* clip by global norm; <= 0 disables clipping */
+    double inv_loss_scale; /* 1 / loss scale applied to the stored gradients */
+} zero_adamw;
+
+/* Device-resident step state (64 bytes, 8-byte aligned).  The caller
+ * zero-initialises it once; zero_adam_step then advances `step` and fills the
+ * per-step scalars (rounded once from fp64) that its element kernel reads. */
+typedef struct {
+    uint64_t step;     /* number of steps taken (not advanced by skipped steps) */
+    uint32_t skip;     /* 1 if the last call skipped (overflow) */
+    uint32_t pad0;
+    double coef;       /* clip coefficient of the last step */
+    float grad_mult;   /* inv_loss_scale * coef */
+    float step_size;   /* lr / (1 - beta1^t) */
+    float inv_sqrt_bc2; /* 1 / sqrt(1 - beta2^t) */
+    float beta1, one_minus_beta1, beta2, one_minus_beta2, eps;
+    float decay;       /* lr * weight_decay */
+    uint32_t pad1;
+} zero_adam_state_t;
+
+/* [P2] ZeRO-DP Stage 1/2: each rank updates only its own part of the
+ * optimizer state, once, at the end of the step ([P2] 考察); [P2] memory
+ * accounting fixes the arrays: 16-bit params and grads, fp32 master,
+ * momentum and variance; [P4] 显存背景 names the optimizer AdamW.
+ * For every element i < n of the shard:
+ *   g  = grad[i] * inv_loss_scale * coef
+ *   m  = beta1 m + (1 - beta1) g;   v = beta2 v + (1 - beta2) g^2
+ *   master = master - lr wd master - lr (m / (1 - beta1^t)) /
+ *            (sqrt(v / (1 - beta2^t)) + eps)
+ *   param_out[i] = master rounded to pdt (nearest, ties to even)
+ * with t the advanced step count and coef = min(1, max_grad_norm / ||g||)
+ * (1 when clipping is off or d_stats is NULL), computed in fp64 on the
+ * device from *d_stats.  If d_stats reports overflow, the step is skipped:
+ * nothing is written to the arrays and `step` does not advance.
+ * grad: n 16-bit gradients (gdt); master, exp_avg, exp_avg_sq: n fp32 each,
+ * updated in place; param_out: n 16-bit params (pdt), written.  d_stats:
+ * device result of zero_grad_stats (or NULL: no clipping, never skip);
+ * d_state: device step state.  n == 0 still advances d_state.
+ * Errors: ZERO_EINVAL (NULL hp or d_state, NULL arrays with n > 0, bad
+ * dtypes, lr < 0, beta outside [0, 1), eps <= 0, weight_decay < 0,
+ * inv_loss_scale not finite and positive, NaN max_grad_norm, overlapping
+ * arrays), ZERO_EALIGN, ZERO_EDEVICE. */
+zero_status zero_adam_step(const zero_adamw *hp, const void *grad, zero_dtype gdt, float *master,
+                           float *exp_avg, float *exp_avg_sq, void *param_out, zero_dtype pdt,
+                           uint64_t n, const zero_grad_stats_t *d_stats,
+                           zero_adam_state_t *d_state, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_MI355X_H */

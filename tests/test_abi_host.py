@@ -1,0 +1,214 @@
+"""The C ABI on the host: symbols, planner parity with the oracle (bit-exact),
+and argument validation of the device calls (rejected before any launch).
+No test here touches a GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle
+import zero_sharded_mixed_grads_amd as z
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "zero.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zero_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) == 9, names
+    assert set(names) == set(z.EXPORTS)
+    L = ctypes.CDLL(z.LIB_PATH)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    assert z.status_str(z.ZERO_OK) == "ZERO_OK"
+    assert z.status_str(z.ZERO_ENOSPC) == "ZERO_ENOSPC"
+    assert z.status_str(99) == "ZERO_UNKNOWN"
+
+
+# ------------------------------------------------------------------ planner
+def test_partition_bit_exact_small_grid():
+    for psi in range(0, 301):
+        for nd in range(1, 34):
+            for r in range(nd):
+                assert z.zero_partition(psi, nd, r) == oracle.partition(psi, nd, r)
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.integers(0, (1 << 62)), st.integers(1, (1 << 32) - 1), st.data())
+def test_partition_bit_exact_large(psi, nd, data):
+    r = data.draw(st.integers(0, min(nd - 1, 5000)))
+    r2 = nd - 1 - data.draw(st.integers(0, min(nd - 1, 5000)))
+    for rank in (r, r2):
+        if nd <= 100_000:  # the oracle walks over the preceding ranks
+            assert z.zero_partition(psi, nd, rank) == oracle.partition(psi, nd, rank)
+        b, e = z.zero_partition(psi, nd, rank)
+        q, rem = divmod(psi, nd)
+        assert e - b == q + (rank < rem) and b == q * rank + min(rank, rem)
+
+
+def test_workload_shards():
+    assert z.zero_partition(1 << 20, 4, 0) == (0, 262_144)
+    assert z.zero_partition(7_459_729_408, 8, 3) == (2_797_398_528, 3_729_864_704)
+    assert z.zero_partition(100_291_305_472, 400, 399) == (100_040_577_209, 100_291_305_472)
+
+
+def test_mem_bytes_bit_exact():
+    for stage in range(4):
+        for psi in list(range(0, 50)) + [7_500_000_000, 1_557_611_200, 12_848_143_360]:
+            for nd in (1, 2, 3, 7, 8, 64, 400, 1024):
+                for k in (0, 4, 12, 16):
+                    assert z.zero_mem_bytes(stage, psi, nd, k) == oracle.mem_bytes(stage, psi, nd, k)
+
+
+def test_mem_bytes_overflow_is_an_error():
+    with pytest.raises(z.ZeroError) as e:
+        z.zero_mem_bytes(0, 1 << 62, 1, 12)
+    assert e.value.status == z.ZERO_EINVAL
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.lists(st.integers(0, 60), min_size=1, max_size=15), st.integers(1, 70), st.data())
+def test_bucket_plan_bit_exact(numels, bucket, data):
+    psi = sum(numels)
+    lo = data.draw(st.integers(0, psi))
+    hi = data.draw(st.integers(lo, psi))
+    got = z.zero_bucket_plan(numels, bucket, lo, hi)
+    ref = [(s.bucket, s.tensor, s.src_off, s.dst_off, s.len)
+           for s in oracle.bucket_plan(numels, bucket, lo, hi)]
+    assert got == ref
+
+
+def test_bucket_plan_workload_layout():
+    from synth import CONFIGS
+    cfg = CONFIGS[3]
+    b, e = oracle.partition(cfg.psi, cfg.nd, cfg.rank)
+    B = cfg.bucket_elems
+    nb = -(-cfg.psi // B)
+    assert nb == 15
+    for bi in range(nb):
+        lo, hi = bi * B, min((bi + 1) * B, cfg.psi)
+        got = z.zero_bucket_plan(cfg.numels, B, lo, hi)
+        ref = [(s.bucket, s.tensor, s.src_off, s.dst_off, s.len)
+               for s in oracle.bucket_plan(cfg.numels, B, lo, hi)]
+        assert got == ref
+    assert hi - lo == 459_729_408
+    shard = z.zero_bucket_plan(cfg.numels, B, b, e)
+    assert {s[0] for s in shard} == {5, 6, 7}
+
+
+def test_bucket_plan_capacity_and_errors():
+    segs = z.zero_bucket_plan([5, 5, 5], 4, 0, 15)
+    assert len(segs) == 6
+    with pytest.raises(z.ZeroError) as e:
+        z.zero_bucket_plan([5, 5, 5], 4, 0, 15, cap=3)
+    assert e.value.status == z.ZERO_ENOSPC
+    for args in ([5], 0, 0, 5), ([5], 2, 3, 2), ([5], 2, 0, 6):
+        with pytest.raises(z.ZeroError) as e:
+            z.zero_bucket_plan(*args)
+        assert e.value.status == z.ZERO_EINVAL
+    assert z.zero_bucket_plan([0, 0], 3, 0, 0) == []
+
+
+def test_planner_errors():
+    for args in ((10, 0, 0), (10, 3, 3)):
+        with pytest.raises(z.ZeroError) as e:
+            z.zero_partition(*args)
+        assert e.value.status == z.ZERO_EINVAL
+    for args in ((4, 10, 1, 12), (1, 10, 0, 12)):
+        with pytest.raises(z.ZeroError) as e:
+            z.zero_mem_bytes(*args)
+        assert e.value.status == z.ZERO_EINVAL
+    assert "nd" in z.lib().zero_last_error().decode()
+
+
+# ---------------------------------------------- device-call validation (host)
+FAKE = 0x7F0000000000  # a 256-byte aligned address; never dereferenced
+
+
+def _status(fn, *args):
+    try:
+        fn(*args)
+    except z.ZeroError as e:
+        return e.status
+    return z.ZERO_OK
+
+
+def test_adam_step_validation():
+    hp = z.adamw()
+    n = 1024
+    g, th, m, v, p = FAKE, FAKE + (1 << 20), FAKE + (2 << 20), FAKE + (3 << 20), FAKE + (4 << 20)
+    stats, state = FAKE + (5 << 20), FAKE + (5 << 20) + 256
+    ok = (hp, g, "f16", th, m, v, p, "f16", n, stats, state, 0)
+
+    def call(**kw):
+        a = list(ok)
+        names = ["hp", "g", "gdt", "th", "m", "v", "p", "pdt", "n", "stats", "state", "stream"]
+        for k, val in kw.items():
+            a[names.index(k)] = val
+        return _status(z.zero_adam_step, *a)
+
+    assert call(state=None) == z.ZERO_EINVAL
+    assert call(gdt="f32") == z.ZERO_EINVAL
+    assert call(pdt=7) == z.ZERO_EINVAL
+    assert call(hp=z.adamw(lr=-1.0)) == z.ZERO_EINVAL
+    assert call(hp=z.adamw(beta1=1.0)) == z.ZERO_EINVAL
+    assert call(hp=z.adamw(beta2=-0.1)) == z.ZERO_EINVAL
+    assert call(hp=z.adamw(eps=0.0)) == z.ZERO_EINVAL
+    assert call(hp=z.adamw(weight_decay=-1e-3)) == z.ZERO_EINVAL
+    assert call(hp=z.adamw(inv_loss_scale=0.0)) == z.ZERO_EINVAL
+    assert call(hp=z.adamw(inv_loss_scale=float("inf"))) == z.ZERO_EINVAL
+    assert call(hp=z.adamw(max_grad_norm=float("nan"))) == z.ZERO_EINVAL
+    assert call(m=None) == z.ZERO_EINVAL
+    assert call(th=th + 2) == z.ZERO_EALIGN
+    assert call(g=g + 1) == z.ZERO_EALIGN
+    assert call(p=p + 3) == z.ZERO_EALIGN
+    assert call(state=state + 4) == z.ZERO_EALIGN
+    assert call(m=th + 4 * n - 4) == z.ZERO_EINVAL       # overlaps master
+    assert call(p=g + 2 * n - 2) == z.ZERO_EINVAL        # overlaps grad
+    assert call(stats=v + 8) == z.ZERO_EINVAL            # stats inside v
+
+
+def test_grad_stats_validation():
+    n = 1 << 20
+    need = z.zero_grad_stats_workspace(n)
+    assert need >= 16 and need % 16 == 0
+    assert z.zero_grad_stats_workspace(0) == 16
+    g, ws, st_ = FAKE, FAKE + (4 << 20), FAKE + (8 << 20)
+    assert _status(z.zero_grad_stats, g, "f16", n, 1.0, ws, need - 1, st_, 0) == z.ZERO_ENOSPC
+    assert _status(z.zero_grad_stats, g, "f32", n, 1.0, ws, need, st_, 0) == z.ZERO_EINVAL
+    assert _status(z.zero_grad_stats, g, "f16", n, 0.0, ws, need, st_, 0) == z.ZERO_EINVAL
+    assert _status(z.zero_grad_stats, None, "f16", n, 1.0, ws, need, st_, 0) == z.ZERO_EINVAL
+    assert _status(z.zero_grad_stats, g, "f16", n, 1.0, ws, need, None, 0) == z.ZERO_EINVAL
+    assert _status(z.zero_grad_stats, g + 1, "f16", n, 1.0, ws, need, st_, 0) == z.ZERO_EALIGN
+    assert _status(z.zero_grad_stats, g, "f16", n, 1.0, ws + 8, need, st_, 0) == z.ZERO_EALIGN
+    assert _status(z.zero_grad_stats, g, "f16", n, 1.0, g + 64, need, st_, 0) == z.ZERO_EINVAL
+
+
+def test_flatten_validation():
+    ts = [FAKE, FAKE + (1 << 20), None]
+    numel = [100, 200, 50]
+    dst = FAKE + (8 << 20)
+    assert _status(z.zero_bucket_flatten, ts, numel, "f16", 0, 0, dst, 0) == z.ZERO_OK  # no-op
+    assert _status(z.zero_bucket_flatten, ts, numel, "f16", 300, 51, dst, 0) == z.ZERO_EINVAL
+    assert _status(z.zero_bucket_flatten, ts, numel, "f16", 250, 60, dst, 0) == z.ZERO_EINVAL
+    assert _status(z.zero_bucket_flatten, ts, numel, 9, 0, 10, dst, 0) == z.ZERO_EINVAL
+    assert _status(z.zero_bucket_flatten, ts, numel, "f16", 0, 10, None, 0) == z.ZERO_EINVAL
+    assert _status(z.zero_bucket_flatten, ts, numel, "f16", 0, 10, dst + 1, 0) == z.ZERO_EALIGN
+    assert _status(z.zero_bucket_flatten, ts, numel, "f32", 0, 10, dst + 2, 0) == z.ZERO_EALIGN
+    bad = [FAKE + 2, FAKE + (1 << 20), None]
+    assert _status(z.zero_bucket_flatten, bad, numel, "f32", 0, 10, dst, 0) == z.ZERO_EALIGN
+    # the NULL third tensor intersects the range: rejected before any launch
+    assert _status(z.zero_bucket_flatten, ts, numel, "f16", 290, 20, dst, 0) == z.ZERO_EINVAL
+    # dst inside a source tensor
+    assert _status(z.zero_bucket_flatten, ts, numel, "f16", 0, 10, FAKE + 8, 0) == z.ZERO_EINVAL

@@ -1,0 +1,124 @@
+"""Helpers shared by the GPU parity tests: phase-controlled device buffers
+with canary guard bands, 16-bit ordered distance, and the AdamW comparison
+criteria (per-step bounds scaled by the size of each update's terms)."""
+import numpy as np
+import torch
+
+CANARY16 = 0x5A5A
+CANARY32 = 0x3C3C3C3C
+GUARD = 64  # elements of guard band on each side
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+class Guarded:
+    """A 1-D device buffer of n elements whose first element sits `phase`
+    elements past a 256-byte boundary, with canary-filled guard bands."""
+
+    def __init__(self, n, dtype, phase=0, init=None):
+        self.n, self.phase, self.dtype = n, phase, dtype
+        tdt = {np.uint16: torch.int16, np.float32: torch.float32}[dtype]
+        self.es = 2 if dtype == np.uint16 else 4
+        self.lead = GUARD + phase
+        total = self.lead + n + GUARD
+        can = np.full(total, CANARY16 if self.es == 2 else CANARY32,
+                      dtype=np.uint16 if self.es == 2 else np.uint32)
+        if init is not None:
+            can[self.lead:self.lead + n] = np.asarray(init).view(can.dtype)
+        self.raw = torch.from_numpy(can.view(np.int16 if self.es == 2 else np.float32)).to(dev())
+        assert self.raw.data_ptr() % 256 == 0
+        self.t = self.raw[self.lead:self.lead + n]
+
+    def ptr(self):
+        return self.raw.data_ptr() + self.lead * self.es
+
+    def host(self):
+        a = self.t.cpu().numpy()
+        return a.view(np.uint16) if self.es == 2 else a.view(np.float32)
+
+    def canaries_intact(self):
+        a = self.raw.cpu().numpy().view(np.uint16 if self.es == 2 else np.uint32)
+        c = CANARY16 if self.es == 2 else CANARY32
+        return bool((a[:self.lead] == c).all() and (a[self.lead + self.n:] == c).all())
+
+
+def ordered16(bits):
+    b = np.asarray(bits).astype(np.int64)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+def ulp16_dist(a, b):
+    return np.abs(ordered16(a) - ordered16(b))
+
+
+def check_adam_one_step(hp, s, g_val, th0, m0, v0, th, m, v, th_ref, m_ref, v_ref,
+                        tol=1e-6, label=""):
+    """Per-element bounds of one step from a common state (th0, m0, v0):
+    m within tol of Sm = max(|m'|, b1|m| + (1-b1)|g|), v within tol of |v'|, the
+    master within tol of max(|p'|, (1 - lr wd)|p| + lr (Sm/bc1)/(sqrt(v_hat)+eps)).
+    The momentum's own rounding error is relative to the size of its terms Sm
+    (its two terms may cancel), and it reaches the master through the update,
+    so the master's scale carries Sm rather than |m'|.
+    s: the oracle's step scalars; g_val: the stored gradient values."""
+    g = np.abs(g_val) * hp.inv_loss_scale * s.coef
+    m_scale = np.maximum(np.abs(m_ref), hp.beta1 * np.abs(m0) + (1 - hp.beta1) * g)
+    v_scale = np.abs(v_ref)
+    upd = (m_scale / s.bc1) / (np.sqrt(np.abs(v_ref) / s.bc2) + hp.eps)
+    th_scale = np.maximum(np.abs(th_ref),
+                          (1 - hp.lr * hp.weight_decay) * np.abs(th0) + hp.lr * upd)
+    errs = {}
+    for name, a, r, sc in (("m", m, m_ref, m_scale), ("v", v, v_ref, v_scale),
+                           ("master", th, th_ref, th_scale)):
+        d = np.abs(a.astype(np.float64) - r.astype(np.float64))
+        ok = d <= tol * sc
+        if not ok.all():
+            i = int(np.argmax(~ok))
+            raise AssertionError(f"{label} {name}[{i}]: gpu {a[i]!r} ref {r[i]!r} "
+                                 f"err {d[i]:.3e} bound {tol * sc[i]:.3e}")
+        with np.errstate(divide="ignore", invalid="ignore"):
+            errs[name] = float(np.nanmax(np.where(sc > 0, d / sc, 0.0))) if d.size else 0.0
+    return errs
+
+
+class FreeRunScales:
+    """Shadow recursions that bound how far two independently computed AdamW
+    trajectories may drift: M_t = b1 M + (1 - b1)|g_t| for the momentum,
+    T_t = (1 - lr wd) T + lr (M_t/bc1)/(sqrt(v_hat)+eps) for the master
+    (T_0 = |p_0|); the variance has no cancellation and is compared relative
+    to itself."""
+
+    def __init__(self, hp, th0):
+        self.hp = hp
+        self.M = np.zeros(th0.size)
+        self.T = np.abs(th0.astype(np.float64))
+
+    def update(self, s, g_val, m_ref, v_ref):
+        hp = self.hp
+        g = np.abs(g_val) * hp.inv_loss_scale * s.coef
+        self.M = hp.beta1 * self.M + (1 - hp.beta1) * g
+        upd = (np.maximum(self.M, np.abs(m_ref)) / s.bc1) / \
+            (np.sqrt(np.abs(v_ref) / s.bc2) + hp.eps)
+        self.T = (1 - hp.lr * hp.weight_decay) * self.T + hp.lr * upd
+
+    def check(self, th, m, v, th_ref, m_ref, v_ref, tol=1e-5, label=""):
+        out = {}
+        for name, a, r, sc in (("m", m, m_ref, np.maximum(self.M, np.abs(m_ref))),
+                               ("v", v, v_ref, np.abs(v_ref)),
+                               ("master", th, th_ref, np.maximum(self.T, np.abs(th_ref)))):
+            d = np.abs(a.astype(np.float64) - r.astype(np.float64))
+            ok = d <= tol * sc
+            if not ok.all():
+                i = int(np.argmax(~ok))
+                raise AssertionError(f"{label} free-running {name}[{i}]: gpu {a[i]!r} "
+                                     f"ref {r[i]!r} err {d[i]:.3e} bound {tol * sc[i]:.3e}")
+            with np.errstate(divide="ignore", invalid="ignore"):
+                out[name] = float(np.nanmax(np.where(sc > 0, d / sc, 0.0))) if d.size else 0.0
+        return out
+
+
+def progress(msg):
+    import sys
+    sys.__stderr__.write(f"    [progress] {msg}\n")
+    sys.__stderr__.flush()

@@ -1,0 +1,213 @@
+"""Python binding of libzero_mi355x: the shard-local mixed-precision AdamW
+step of ZeRO-DP for AMD MI355X.
+
+Argument marshalling only: every function forwards to the C entry point of
+the same name in ``libzero_mi355x.so`` (declared in ``include/zero.h``).
+Tensors are accepted where the C call takes a device pointer (their
+``data_ptr()`` is passed); the stream defaults to torch's current stream.
+Nothing here computes any part of the step, and there is no fallback: if the
+library is missing, importing a device call raises.
+"""
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+import torch  # loads the HIP runtime that the library then binds to
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzero_mi355x.so")
+
+ZERO_OK, ZERO_EINVAL, ZERO_ENOSPC, ZERO_EALIGN, ZERO_EDEVICE = range(5)
+ZERO_F32, ZERO_F16, ZERO_BF16 = range(3)
+
+_DTYPES = {"f32": ZERO_F32, "f16": ZERO_F16, "bf16": ZERO_BF16,
+           torch.float32: ZERO_F32, torch.float16: ZERO_F16, torch.bfloat16: ZERO_BF16}
+
+U64, U32, DBL, VP = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_double, ctypes.c_void_p
+
+
+class ZeroError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(detail)
+        self.status = status
+
+
+class Segment(ctypes.Structure):
+    _fields_ = [("bucket", U64), ("tensor", U64), ("src_off", U64), ("dst_off", U64),
+                ("len", U64)]
+
+
+class AdamW(ctypes.Structure):
+    _fields_ = [("lr", DBL), ("beta1", DBL), ("beta2", DBL), ("eps", DBL),
+                ("weight_decay", DBL), ("max_grad_norm", DBL), ("inv_loss_scale", DBL)]
+
+
+class GradStats(ctypes.Structure):  # zero_grad_stats_t, device resident
+    _fields_ = [("sq_norm", DBL), ("overflow", U32), ("pad", U32)]
+
+
+class AdamState(ctypes.Structure):  # zero_adam_state_t, device resident
+    _fields_ = [("step", U64), ("skip", U32), ("pad0", U32), ("coef", DBL),
+                ("grad_mult", ctypes.c_float), ("step_size", ctypes.c_float),
+                ("inv_sqrt_bc2", ctypes.c_float), ("beta1", ctypes.c_float),
+                ("one_minus_beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("one_minus_beta2", ctypes.c_float), ("eps", ctypes.c_float),
+                ("decay", ctypes.c_float), ("pad1", U32)]
+
+
+assert ctypes.sizeof(GradStats) == 16 and ctypes.sizeof(AdamState) == 64
+
+EXPORTS = ("zero_status_str", "zero_last_error", "zero_partition", "zero_mem_bytes",
+           "zero_bucket_plan", "zero_bucket_flatten", "zero_grad_stats_workspace",
+           "zero_grad_stats", "zero_adam_step")
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.zero_status_str.argtypes = [ctypes.c_int]
+        L.zero_status_str.restype = ctypes.c_char_p
+        L.zero_last_error.argtypes = []
+        L.zero_last_error.restype = ctypes.c_char_p
+        L.zero_partition.argtypes = [U64, U32, U32, ctypes.POINTER(U64), ctypes.POINTER(U64)]
+        L.zero_mem_bytes.argtypes = [U32, U64, U32, U32, ctypes.POINTER(U64)]
+        L.zero_bucket_plan.argtypes = [ctypes.POINTER(U64), U32, U64, U64, U64,
+                                       ctypes.POINTER(Segment), U64, ctypes.POINTER(U64)]
+        L.zero_bucket_flatten.argtypes = [ctypes.POINTER(VP), ctypes.POINTER(U64), U32,
+                                          ctypes.c_int, U64, U64, VP, VP]
+        L.zero_grad_stats_workspace.argtypes = [U64, ctypes.POINTER(ctypes.c_size_t)]
+        L.zero_grad_stats.argtypes = [VP, ctypes.c_int, U64, DBL, VP, ctypes.c_size_t, VP, VP]
+        L.zero_adam_step.argtypes = [ctypes.POINTER(AdamW), VP, ctypes.c_int, VP, VP, VP, VP,
+                                     ctypes.c_int, U64, VP, VP, VP]
+        for name in EXPORTS[2:]:
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != ZERO_OK:
+        raise ZeroError(status, lib().zero_last_error().decode())
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dtype(dt) -> int:
+    return _DTYPES[dt] if dt in _DTYPES else int(dt)
+
+
+def status_str(status: int) -> str:
+    return lib().zero_status_str(status).decode()
+
+
+# ------------------------------------------------------------------ planner
+def zero_partition(psi: int, nd: int, rank: int) -> Tuple[int, int]:
+    b, e = U64(), U64()
+    _check(lib().zero_partition(psi, nd, rank, ctypes.byref(b), ctypes.byref(e)))
+    return b.value, e.value
+
+
+def zero_mem_bytes(stage: int, psi: int, nd: int, k: int = 12) -> int:
+    out = U64()
+    _check(lib().zero_mem_bytes(stage, psi, nd, k, ctypes.byref(out)))
+    return out.value
+
+
+def zero_bucket_plan(numel: Sequence[int], bucket_elems: int, range_begin: int,
+                     range_end: int, cap: Optional[int] = None) -> List[Tuple[int, ...]]:
+    """Segments (bucket, tensor, src_off, dst_off, len) of the range."""
+    arr = (U64 * len(numel))(*numel)
+    n = U64()
+    if cap is None:  # ask for the count first
+        st = lib().zero_bucket_plan(arr, len(numel), bucket_elems, range_begin, range_end,
+                                    None, 0, ctypes.byref(n))
+        if st not in (ZERO_OK, ZERO_ENOSPC):
+            _check(st)
+        cap = n.value
+    segs = (Segment * max(cap, 1))()
+    _check(lib().zero_bucket_plan(arr, len(numel), bucket_elems, range_begin, range_end,
+                                  segs, cap, ctypes.byref(n)))
+    return [(s.bucket, s.tensor, s.src_off, s.dst_off, s.len) for s in segs[:n.value]]
+
+
+# ------------------------------------------------------------- device calls
+def zero_bucket_flatten(tensors: Sequence, numel: Optional[Sequence[int]], dtype,
+                        range_begin: int, count: int, dst, stream=None) -> None:
+    """tensors: device tensors or device pointers (None allowed for tensors
+    outside the range); numel defaults to each tensor's numel()."""
+    if numel is None:
+        numel = [t.numel() for t in tensors]
+    ptrs = (VP * len(tensors))(*[_ptr(t) for t in tensors])
+    nums = (U64 * len(numel))(*numel)
+    _check(lib().zero_bucket_flatten(ptrs, nums, len(tensors), _dtype(dtype), range_begin,
+                                     count, _ptr(dst), _stream(stream)))
+
+
+def zero_grad_stats_workspace(n: int) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().zero_grad_stats_workspace(n, ctypes.byref(out)))
+    return out.value
+
+
+def zero_grad_stats(grad, gdtype, n: int, inv_loss_scale: float, workspace, ws_bytes: int,
+                    d_stats, stream=None) -> None:
+    _check(lib().zero_grad_stats(_ptr(grad), _dtype(gdtype), n, inv_loss_scale, _ptr(workspace),
+                                 ws_bytes, _ptr(d_stats), _stream(stream)))
+
+
+def zero_adam_step(hp: AdamW, grad, gdtype, master, exp_avg, exp_avg_sq, param_out, pdtype,
+                   n: int, d_stats, d_state, stream=None) -> None:
+    _check(lib().zero_adam_step(ctypes.byref(hp), _ptr(grad), _dtype(gdtype), _ptr(master),
+                                _ptr(exp_avg), _ptr(exp_avg_sq), _ptr(param_out), _dtype(pdtype),
+                                n, _ptr(d_stats), _ptr(d_state), _stream(stream)))
+
+
+# ----------------------------------------------- device struct conveniences
+def new_grad_stats(device) -> torch.Tensor:
+    """A zeroed device buffer for one zero_grad_stats_t."""
+    return torch.zeros(ctypes.sizeof(GradStats), dtype=torch.uint8, device=device)
+
+
+def new_adam_state(device) -> torch.Tensor:
+    """A zeroed device buffer for one zero_adam_state_t (step 0)."""
+    return torch.zeros(ctypes.sizeof(AdamState), dtype=torch.uint8, device=device)
+
+
+def new_workspace(n: int, device) -> torch.Tensor:
+    return torch.empty(max(zero_grad_stats_workspace(n), 16), dtype=torch.uint8, device=device)
+
+
+def read_grad_stats(buf: torch.Tensor) -> GradStats:
+    """Synchronising copy of a device zero_grad_stats_t."""
+    return GradStats.from_buffer_copy(bytes(buf.cpu().numpy()))
+
+
+def read_adam_state(buf: torch.Tensor) -> AdamState:
+    """Synchronising copy of a device zero_adam_state_t."""
+    return AdamState.from_buffer_copy(bytes(buf.cpu().numpy()))
+
+
+def adamw(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_grad_norm=0.0,
+          inv_loss_scale=1.0) -> AdamW:
+    return AdamW(lr, beta1, beta2, eps, weight_decay, max_grad_norm, inv_loss_scale)

@@ -1,0 +1,53 @@
+"""Builds libzero_mi355x.so in-tree with hipcc for gfx950.
+
+Two translation units: the host planner (C++) and the HIP device path.
+All HIP code is compiled without packed-fp32 instructions and without
+denormal flushing.
+"""
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libzero_mi355x.so")
+BUILD_DIR = os.path.join(ROOT, "_build")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}", f"-I{CSRC}"]
+DEVICE = [f"--offload-arch={ARCH}", "-mcode-object-version=5", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-fno-gpu-flush-denormals-to-zero", "-Wno-unused-command-line-argument"]
+
+SOURCES = ["zero_host.cpp", "zero_kernels.hip"]
+
+
+def _run(cmd):
+    print("+", " ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every source and link the shared library (always rebuilds)."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        path = os.path.join(CSRC, src)
+        obj = os.path.join(BUILD_DIR, src + ".o")
+        if src.endswith(".hip"):
+            _run([HIPCC, *COMMON, *DEVICE, "-x", "hip", "-c", path, "-o", obj])
+        else:
+            _run([HIPCC, *COMMON, "-x", "c++", "-c", path, "-o", obj])
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build()
+    sys.exit(0)

@@ -1,0 +1,826 @@
+// Device path of libzero_mi355x for AMD MI355X (gfx950, CDNA4, wave64).
+//
+// Three HBM-bound streaming kernels and two single-block epilogues:
+//   flatten_segments  - list-order gather of tensors into a contiguous buffer
+//                       ("ZeRO: Memory Optimizations Toward Training Trillion
+//                       Parameter Models", paper summary page, section ZeRO-R
+//                       > CB: constant-size fused buffers)
+//   stats_pass1/2     - overflow flag and fp64 squared norm of a 16-bit
+//                       gradient shard, fixed-order two-pass reduction
+//   adam_scalars      - per-step scalars in fp64 (skip, clip, bias corrections)
+//   adamw_stream      - the fused AdamW update of one rank's shard (same page,
+//                       section ZeRO-DP, Stage 1: each rank updates only its
+//                       1/Nd of the optimizer state; section メモリ消費の定量化:
+//                       16-bit params and grads, fp32 master, momentum and
+//                       variance), 28 bytes of HBM traffic per element.
+//
+// Memory access rules used throughout: every global load and store is
+// naturally aligned (16-byte vectors on 16-byte boundaries, dwords on 4,
+// shorts on 2).  A 16-bit stream whose 16-byte phase differs from the fp32
+// streams is realigned in registers: loads read the two aligned 16-byte lines
+// that cover the 8 wanted elements and funnel-shift them with v_alignbyte;
+// stores split the 8 elements into naturally aligned pieces.  An aligned line
+// that holds at least one byte of a live buffer lies inside a mapped page, so
+// the over-read of such a line never faults; over-read bytes are discarded.
+// No scalar-cache writes, no float atomics: results are bit-reproducible.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <vector>
+
+#include "zero_internal.h"
+
+using zero::fail;
+
+namespace {
+
+constexpr int kBlock = 256;  // 4 waves of 64 lanes
+
+// ------------------------------------------------------------ 16-bit helpers
+template <bool BF16>
+__device__ __forceinline__ float to_f32(uint32_t h)  // h: bits in the low half
+{
+    if constexpr (BF16) {
+        return __uint_as_float(h << 16);
+    } else {
+        _Float16 x;
+        uint16_t b = (uint16_t)h;
+        __builtin_memcpy(&x, &b, 2);
+        return (float)x;  // exact widening
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float hi_to_f32(uint32_t w)  // the upper half of a dword
+{
+    if constexpr (BF16)
+        return __uint_as_float(w & 0xffff0000u);
+    else
+        return to_f32<false>(w >> 16);
+}
+
+// Round to nearest, ties to even.
+template <bool BF16>
+__device__ __forceinline__ uint32_t from_f32(float x)
+{
+    if constexpr (BF16) {
+        uint32_t u = __float_as_uint(x);
+        if ((u & 0x7fffffffu) > 0x7f800000u)  // NaN: keep it a (quiet) NaN
+            return (u >> 16) | 0x40u;
+        u += 0x7fffu + ((u >> 16) & 1u);
+        return u >> 16;
+    } else {
+        _Float16 h = (_Float16)x;  // v_cvt_f16_f32, round-to-nearest-even mode
+        uint16_t b;
+        __builtin_memcpy(&b, &h, 2);
+        return b;
+    }
+}
+
+// Bytes [SB, SB + 16) of the 32-byte concatenation lo:hi (SB even).
+template <int SB>
+__device__ __forceinline__ uint4 shift_lines(const uint4 &lo, const uint4 &hi)
+{
+    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    constexpr int q = SB / 4, r = SB % 4;
+    uint4 o;
+    if constexpr (r == 0) {
+        o.x = w[q]; o.y = w[q + 1]; o.z = w[q + 2]; o.w = w[q + 3];
+    } else {
+        o.x = __builtin_amdgcn_alignbyte(w[q + 1], w[q], r);
+        o.y = __builtin_amdgcn_alignbyte(w[q + 2], w[q + 1], r);
+        o.z = __builtin_amdgcn_alignbyte(w[q + 3], w[q + 2], r);
+        o.w = __builtin_amdgcn_alignbyte(w[q + 4], w[q + 3], r);
+    }
+    return o;
+}
+
+// Runtime-uniform byte shift (0..14, even) dispatched to the templates.
+__device__ __forceinline__ uint4 shift_lines_rt(const uint4 &lo, const uint4 &hi, uint32_t sb)
+{
+    switch (sb) {
+    case 0: return lo;
+    case 2: return shift_lines<2>(lo, hi);
+    case 4: return shift_lines<4>(lo, hi);
+    case 6: return shift_lines<6>(lo, hi);
+    case 8: return shift_lines<8>(lo, hi);
+    case 10: return shift_lines<10>(lo, hi);
+    case 12: return shift_lines<12>(lo, hi);
+    default: return shift_lines<14>(lo, hi);
+    }
+}
+
+// Stores halves h[0..COUNT) into slots [SLOT, SLOT + COUNT) of the aligned
+// 16-byte line at `line`, as naturally aligned short/dword/dwordx2/dwordx4.
+template <int SLOT, int COUNT>
+__device__ __forceinline__ void store_run(uint16_t *line, const uint32_t *h)
+{
+    if constexpr (COUNT <= 0) {
+        return;
+    } else if constexpr ((SLOT & 1) || COUNT == 1) {
+        line[SLOT] = (uint16_t)h[0];
+        store_run<SLOT + 1, COUNT - 1>(line, h + 1);
+    } else if constexpr (SLOT % 8 == 0 && COUNT >= 8) {
+        *reinterpret_cast<uint4 *>(line + SLOT) =
+            make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16);
+        store_run<SLOT + 8, COUNT - 8>(line, h + 8);
+    } else if constexpr (SLOT % 4 == 0 && COUNT >= 4) {
+        *reinterpret_cast<uint2 *>(line + SLOT) = make_uint2(h[0] | h[1] << 16, h[2] | h[3] << 16);
+        store_run<SLOT + 4, COUNT - 4>(line, h + 4);
+    } else {
+        *reinterpret_cast<uint32_t *>(line + SLOT) = h[0] | h[1] << 16;
+        store_run<SLOT + 2, COUNT - 2>(line, h + 2);
+    }
+}
+
+// Eight halves whose first element sits at slot PH of the aligned line
+// `line`: slots PH..7 of this line and 0..PH-1 of the next one.
+template <int PH>
+__device__ __forceinline__ void store_phased(uint16_t *line, const uint32_t *h)
+{
+    store_run<PH, 8 - PH>(line, h);
+    store_run<0, PH>(line + 8, h + 8 - PH);
+}
+
+__device__ __forceinline__ void store_phased_rt(uint16_t *line, const uint32_t *h, uint32_t ph)
+{
+    switch (ph) {
+    case 1: store_phased<1>(line, h); break;
+    case 2: store_phased<2>(line, h); break;
+    case 3: store_phased<3>(line, h); break;
+    case 4: store_phased<4>(line, h); break;
+    case 5: store_phased<5>(line, h); break;
+    case 6: store_phased<6>(line, h); break;
+    case 7: store_phased<7>(line, h); break;
+    default: store_run<0, 8>(line, h); break;
+    }
+}
+
+// fp64 wave reduction over 64 lanes (fixed butterfly order).
+__device__ __forceinline__ double wave_sum(double x)
+{
+    for (int o = 32; o > 0; o >>= 1)
+        x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+__device__ __forceinline__ uint32_t wave_or(uint32_t x)
+{
+    for (int o = 32; o > 0; o >>= 1)
+        x |= __shfl_xor(x, o, 64);
+    return x;
+}
+
+// ================================================================ flatten
+constexpr int kMaxSegs = 96;         // segments per launch (kernel-argument table)
+constexpr int kFlatChunksPerThread = 4;
+constexpr uint64_t kFlatTileChunks = (uint64_t)kBlock * kFlatChunksPerThread;
+constexpr int kFlatMaxBlocks = 2048;
+
+struct FlatArgs {
+    char *dst;                     // element 0 of the destination range
+    uint32_t n_segs;
+    uint32_t dst_phase;            // (dst address mod 16) / element size
+    uint64_t seg_lo[kMaxSegs + 1]; // destination element offset of each segment
+    uint64_t tile_lo[kMaxSegs + 1];// first tile of each segment; last = total
+    const char *src[kMaxSegs];     // address of each segment's first source element
+};
+
+template <int ES, int SB>
+__device__ __forceinline__ void flatten_full_chunks(const char *src_line0, char *dst_line0,
+                                                    uint64_t c_beg, uint64_t c_end)
+{
+    // chunk c (relative to the segment's first full chunk) reads the aligned
+    // source lines c and c+1 (shifted by SB bytes) and writes destination line c
+    uint4 lo[kFlatChunksPerThread], hi[kFlatChunksPerThread];
+#pragma unroll
+    for (int j = 0; j < kFlatChunksPerThread; ++j) {
+        const uint64_t c = c_beg + (uint64_t)j * kBlock + threadIdx.x;
+        if (c < c_end) {
+            const uint4 *s = reinterpret_cast<const uint4 *>(src_line0) + c;
+            lo[j] = s[0];
+            if constexpr (SB != 0)
+                hi[j] = s[1];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kFlatChunksPerThread; ++j) {
+        const uint64_t c = c_beg + (uint64_t)j * kBlock + threadIdx.x;
+        if (c < c_end) {
+            uint4 o;
+            if constexpr (SB == 0)
+                o = lo[j];
+            else
+                o = shift_lines<SB>(lo[j], hi[j]);
+            reinterpret_cast<uint4 *>(dst_line0)[c] = o;
+        }
+    }
+}
+
+template <int ES>
+__global__ void __launch_bounds__(kBlock) flatten_segments(FlatArgs a)
+{
+    constexpr uint64_t V = 16 / ES;  // elements per 16-byte line
+    const uint64_t total_tiles = a.tile_lo[a.n_segs];
+    for (uint64_t tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
+        // segment of this tile: largest s with tile_lo[s] <= tile (uniform)
+        uint32_t lo = 0, hi = a.n_segs;
+        while (hi - lo > 1) {
+            const uint32_t mid = (lo + hi) / 2;
+            if (a.tile_lo[mid] <= tile) lo = mid; else hi = mid;
+        }
+        const uint32_t s = lo;
+        const uint64_t e_lo = a.seg_lo[s], e_hi = a.seg_lo[s + 1];
+        const uint64_t ph = a.dst_phase;
+        // full destination lines inside the segment: [c0, c1) in line units
+        const uint64_t c0 = (e_lo + ph + V - 1) / V, c1 = (e_hi + ph) / V;
+        const bool has_full = c1 > c0;
+        const uint64_t k = tile - a.tile_lo[s];
+        const char *src = a.src[s];
+        if (k == 0) {
+            // partial lines at both ends, element by element
+            const uint64_t head_end = has_full ? c0 * V - ph : e_hi;
+            const uint64_t tail_beg = has_full ? c1 * V - ph : e_hi;
+            const uint64_t n_head = head_end - e_lo, n_tail = e_hi - tail_beg;
+            const uint64_t i = threadIdx.x;
+            if (i < n_head + n_tail) {
+                const uint64_t e = i < n_head ? e_lo + i : tail_beg + (i - n_head);
+                if constexpr (ES == 2)
+                    reinterpret_cast<uint16_t *>(a.dst)[e] =
+                        reinterpret_cast<const uint16_t *>(src)[e - e_lo];
+                else
+                    reinterpret_cast<uint32_t *>(a.dst)[e] =
+                        reinterpret_cast<const uint32_t *>(src)[e - e_lo];
+            }
+        }
+        if (!has_full)
+            continue;
+        const uint64_t t_beg = k * kFlatTileChunks;
+        const uint64_t t_end = (t_beg + kFlatTileChunks < c1 - c0) ? t_beg + kFlatTileChunks : c1 - c0;
+        // first full line's source bytes and their 16-byte phase (uniform)
+        const uintptr_t s0 = (uintptr_t)(src + (c0 * V - ph - e_lo) * ES);
+        const uint32_t sb = (uint32_t)(s0 & 15u);
+        const char *src_line0 = (const char *)(s0 - sb);
+        char *dst_line0 = a.dst + (c0 * V - ph) * ES;
+        switch (sb) {
+        case 0: flatten_full_chunks<ES, 0>(src_line0, dst_line0, t_beg, t_end); break;
+        case 4: flatten_full_chunks<ES, 4>(src_line0, dst_line0, t_beg, t_end); break;
+        case 8: flatten_full_chunks<ES, 8>(src_line0, dst_line0, t_beg, t_end); break;
+        case 12: flatten_full_chunks<ES, 12>(src_line0, dst_line0, t_beg, t_end); break;
+        default:
+            if constexpr (ES == 2) {
+                switch (sb) {
+                case 2: flatten_full_chunks<ES, 2>(src_line0, dst_line0, t_beg, t_end); break;
+                case 6: flatten_full_chunks<ES, 6>(src_line0, dst_line0, t_beg, t_end); break;
+                case 10: flatten_full_chunks<ES, 10>(src_line0, dst_line0, t_beg, t_end); break;
+                default: flatten_full_chunks<ES, 14>(src_line0, dst_line0, t_beg, t_end); break;
+                }
+            }
+            break;
+        }
+    }
+}
+
+// ============================================================ grad stats
+constexpr int kStatsUnroll = 4;
+constexpr int kStatsMaxBlocks = 2048;
+
+struct Partial {
+    double sum;
+    uint32_t flag;
+    uint32_t pad;
+};
+
+// Blocks of pass 1 for n gradients: a function of n only, so the result is
+// reproducible for a given n whatever the buffer's address.
+uint32_t stats_blocks(uint64_t n)
+{
+    const uint64_t per_block = (uint64_t)kBlock * 8 * kStatsUnroll * 4;
+    uint64_t b = (n + per_block - 1) / per_block;
+    if (b < 1) b = 1;
+    if (b > kStatsMaxBlocks) b = kStatsMaxBlocks;
+    return (uint32_t)b;
+}
+
+template <bool BF16>
+__device__ __forceinline__ uint32_t nonfinite2(uint32_t w)  // both halves of a dword
+{
+    constexpr uint32_t E = BF16 ? 0x7f80u : 0x7c00u;
+    return ((w & E) == E) | (((w >> 16) & E) == E);
+}
+
+template <bool BF16>
+__device__ __forceinline__ void accum2(uint32_t w, double &acc)
+{
+    const double a = (double)to_f32<BF16>(w & 0xffffu);
+    const double b = (double)hi_to_f32<BF16>(w);
+    acc = fma(a, a, acc);  // squares of 16-bit values are exact in fp64
+    acc = fma(b, b, acc);
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(kBlock)
+    stats_pass1(const uint16_t *g, uint64_t head, uint64_t nchunks, uint64_t tail_beg, uint64_t n,
+                Partial *part)
+{
+    double acc = 0.0;
+    uint32_t flag = 0;
+    const uint4 *lines = reinterpret_cast<const uint4 *>(g + head);
+    const uint64_t stride = (uint64_t)gridDim.x * kBlock;
+    for (uint64_t base = (uint64_t)blockIdx.x * kBlock + threadIdx.x; base < nchunks;
+         base += stride * kStatsUnroll) {
+        uint4 w[kStatsUnroll];
+#pragma unroll
+        for (int j = 0; j < kStatsUnroll; ++j) {
+            const uint64_t c = base + j * stride;
+            w[j] = c < nchunks ? lines[c] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < kStatsUnroll; ++j) {
+            flag |= nonfinite2<BF16>(w[j].x) | nonfinite2<BF16>(w[j].y) |
+                    nonfinite2<BF16>(w[j].z) | nonfinite2<BF16>(w[j].w);
+            accum2<BF16>(w[j].x, acc);
+            accum2<BF16>(w[j].y, acc);
+            accum2<BF16>(w[j].z, acc);
+            accum2<BF16>(w[j].w, acc);
+        }
+    }
+    // elements outside the aligned lines: [0, head) and [tail_beg, n)
+    const uint64_t gid = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
+    const uint64_t n_edge = head + (n - tail_beg);
+    if (gid < n_edge) {
+        const uint32_t h = g[gid < head ? gid : tail_beg + (gid - head)];
+        flag |= nonfinite2<BF16>(h);
+        const double x = (double)to_f32<BF16>(h);
+        acc = fma(x, x, acc);
+    }
+    // block reduction in a fixed order
+    __shared__ double s_sum[kBlock / 64];
+    __shared__ uint32_t s_flag[kBlock / 64];
+    acc = wave_sum(acc);
+    flag = wave_or(flag);
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    if (lane == 0) {
+        s_sum[wave] = acc;
+        s_flag[wave] = flag;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double s = 0.0;
+        uint32_t f = 0;
+        for (int i = 0; i < kBlock / 64; ++i) {
+            s += s_sum[i];
+            f |= s_flag[i];
+        }
+        part[blockIdx.x] = Partial{s, f, 0};
+    }
+}
+
+__global__ void __launch_bounds__(kBlock)
+    stats_pass2(const Partial *part, uint32_t n_part, double inv_scale_sq, zero_grad_stats_t *out)
+{
+    double s = 0.0;
+    uint32_t f = 0;
+    for (uint32_t i = threadIdx.x; i < n_part; i += kBlock) {
+        s += part[i].sum;
+        f |= part[i].flag;
+    }
+    __shared__ double s_sum[kBlock / 64];
+    __shared__ uint32_t s_flag[kBlock / 64];
+    s = wave_sum(s);
+    f = wave_or(f);
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    if (lane == 0) {
+        s_sum[wave] = s;
+        s_flag[wave] = f;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double t = 0.0;
+        uint32_t ff = 0;
+        for (int i = 0; i < kBlock / 64; ++i) {
+            t += s_sum[i];
+            ff |= s_flag[i];
+        }
+        out->sq_norm = t * inv_scale_sq;
+        out->overflow = ff ? 1u : 0u;
+        out->pad = 0;
+    }
+}
+
+// ================================================================= AdamW
+// Per-step scalars, computed once in fp64 by one thread and rounded once.
+__global__ void adam_scalars(zero_adamw hp, const zero_grad_stats_t *stats,
+                             zero_adam_state_t *st)
+{
+    if (threadIdx.x != 0 || blockIdx.x != 0)
+        return;
+    const uint32_t overflow = stats ? stats->overflow : 0u;
+    if (overflow) {  // skipped step: nothing advances
+        st->skip = 1;
+        return;
+    }
+    const uint64_t t = st->step + 1;
+    double coef = 1.0;
+    if (stats && hp.max_grad_norm > 0.0) {
+        const double sq = stats->sq_norm;
+        if (sq > 0.0) {
+            const double norm = sqrt(sq);
+            if (hp.max_grad_norm < norm)
+                coef = hp.max_grad_norm / norm;
+        }
+    }
+    const double bc1 = 1.0 - pow(hp.beta1, (double)t);
+    const double bc2 = 1.0 - pow(hp.beta2, (double)t);
+    st->step = t;
+    st->skip = 0;
+    st->coef = coef;
+    st->grad_mult = (float)(hp.inv_loss_scale * coef);
+    st->step_size = (float)(hp.lr / bc1);
+    st->inv_sqrt_bc2 = (float)(1.0 / sqrt(bc2));
+    st->beta1 = (float)hp.beta1;
+    st->one_minus_beta1 = (float)(1.0 - hp.beta1);
+    st->beta2 = (float)hp.beta2;
+    st->one_minus_beta2 = (float)(1.0 - hp.beta2);
+    st->eps = (float)hp.eps;
+    st->decay = (float)(hp.lr * hp.weight_decay);
+}
+
+struct AdamArgs {
+    const uint16_t *g;
+    float *master, *m, *v;
+    uint16_t *p;
+    const zero_adam_state_t *st;
+    uint64_t n;
+    uint64_t head;     // elements [0, head) go element by element
+    uint64_t nchunks;  // then nchunks chunks of 8 elements
+    uint32_t g_phase;  // slot (0..7) of element `head` of g within its 16-byte line
+    uint32_t p_phase;  // same for p
+};
+
+struct Coeffs {
+    float grad_mult, step_size, inv_sqrt_bc2, b1, omb1, b2, omb2, eps, decay;
+};
+
+__device__ __forceinline__ void adamw_elem(const Coeffs &k, float graw, float &th, float &m,
+                                           float &v)
+{
+    const float g = graw * k.grad_mult;
+    const float m1 = fmaf(k.b1, m, k.omb1 * g);
+    const float v1 = fmaf(k.b2, v, (k.omb2 * g) * g);
+    const float den = fmaf(sqrtf(v1), k.inv_sqrt_bc2, k.eps);
+    const float th1 = fmaf(-k.decay, th, th);
+    th = fmaf(-k.step_size, m1 / den, th1);
+    m = m1;
+    v = v1;
+}
+
+constexpr int kAdamUnroll = 2;
+constexpr int kAdamMaxBlocks = 2048;
+
+template <bool GBF16, bool PBF16, bool G_ALIGNED, bool P_ALIGNED>
+__global__ void __launch_bounds__(kBlock) adamw_stream(AdamArgs a)
+{
+    const zero_adam_state_t *st = a.st;
+    if (st->skip)
+        return;
+    const Coeffs k{st->grad_mult, st->step_size, st->inv_sqrt_bc2, st->beta1, st->one_minus_beta1,
+                   st->beta2, st->one_minus_beta2, st->eps, st->decay};
+
+    // aligned views of the body [head, head + 8 nchunks)
+    float4 *th4 = reinterpret_cast<float4 *>(a.master + a.head);
+    float4 *m4 = reinterpret_cast<float4 *>(a.m + a.head);
+    float4 *v4 = reinterpret_cast<float4 *>(a.v + a.head);
+    const uint4 *gl = reinterpret_cast<const uint4 *>(a.g + a.head - a.g_phase);
+    uint16_t *pl = a.p + a.head - a.p_phase;  // aligned line holding element `head`
+    const uint32_t gsb = 2 * a.g_phase;
+
+    const uint64_t stride = (uint64_t)gridDim.x * kBlock;
+    for (uint64_t base = (uint64_t)blockIdx.x * kBlock + threadIdx.x; base < a.nchunks;
+         base += stride * kAdamUnroll) {
+        uint4 gw[kAdamUnroll];
+        float4 th[kAdamUnroll][2], mm[kAdamUnroll][2], vv[kAdamUnroll][2];
+#pragma unroll
+        for (int j = 0; j < kAdamUnroll; ++j) {
+            const uint64_t c = base + j * stride;
+            if (c < a.nchunks) {
+                if constexpr (G_ALIGNED) {
+                    gw[j] = gl[c];
+                } else {
+                    const uint4 lo = gl[c], hi = gl[c + 1];
+                    gw[j] = shift_lines_rt(lo, hi, gsb);
+                }
+                th[j][0] = th4[2 * c]; th[j][1] = th4[2 * c + 1];
+                mm[j][0] = m4[2 * c];  mm[j][1] = m4[2 * c + 1];
+                vv[j][0] = v4[2 * c];  vv[j][1] = v4[2 * c + 1];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kAdamUnroll; ++j) {
+            const uint64_t c = base + j * stride;
+            if (c < a.nchunks) {
+                const uint32_t gws[4] = {gw[j].x, gw[j].y, gw[j].z, gw[j].w};
+                float *t = reinterpret_cast<float *>(th[j]);
+                float *mv = reinterpret_cast<float *>(mm[j]);
+                float *vw = reinterpret_cast<float *>(vv[j]);
+                uint32_t ph[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t w = gws[e / 2];
+                    const float graw = (e & 1) ? hi_to_f32<GBF16>(w) : to_f32<GBF16>(w & 0xffffu);
+                    adamw_elem(k, graw, t[e], mv[e], vw[e]);
+                    ph[e] = from_f32<PBF16>(t[e]);
+                }
+                th4[2 * c] = th[j][0]; th4[2 * c + 1] = th[j][1];
+                m4[2 * c] = mm[j][0];  m4[2 * c + 1] = mm[j][1];
+                v4[2 * c] = vv[j][0];  v4[2 * c + 1] = vv[j][1];
+                if constexpr (P_ALIGNED)
+                    store_run<0, 8>(pl + 8 * c, ph);
+                else
+                    store_phased_rt(pl + 8 * c, ph, a.p_phase);
+            }
+        }
+    }
+    // elements outside the body, one per thread: [0, head) and the tail
+    const uint64_t body_end = a.head + 8 * a.nchunks;
+    const uint64_t n_edge = a.head + (a.n - body_end);
+    for (uint64_t i = (uint64_t)blockIdx.x * kBlock + threadIdx.x; i < n_edge; i += stride) {
+        const uint64_t e = i < a.head ? i : body_end + (i - a.head);
+        float t = a.master[e], mv = a.m[e], vw = a.v[e];
+        adamw_elem(k, to_f32<GBF16>(a.g[e]), t, mv, vw);
+        a.master[e] = t;
+        a.m[e] = mv;
+        a.v[e] = vw;
+        a.p[e] = (uint16_t)from_f32<PBF16>(t);
+    }
+}
+
+// ------------------------------------------------------------ host helpers
+inline bool aligned(const void *p, uintptr_t k) { return ((uintptr_t)p & (k - 1)) == 0; }
+
+inline bool overlap(const void *a, uint64_t an, const void *b, uint64_t bn)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return an && bn && x < y + bn && y < x + an;
+}
+
+zero_status launch_status(const char *what)
+{
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(ZERO_EDEVICE, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ZERO_OK;
+}
+
+inline uint32_t grid_for(uint64_t work_items, uint64_t per_block, uint32_t max_blocks)
+{
+    uint64_t b = (work_items + per_block - 1) / per_block;
+    if (b < 1) b = 1;
+    if (b > max_blocks) b = max_blocks;
+    return (uint32_t)b;
+}
+
+template <int ES>
+zero_status flatten_launch(FlatArgs &a, hipStream_t stream)
+{
+    const uint32_t grid = grid_for(a.tile_lo[a.n_segs], 1, kFlatMaxBlocks);
+    hipLaunchKernelGGL(flatten_segments<ES>, dim3(grid), dim3(kBlock), 0, stream, a);
+    return launch_status("zero_bucket_flatten");
+}
+
+}  // namespace
+
+// ============================================================== C entry points
+extern "C" zero_status zero_bucket_flatten(const void *const *tensor_ptrs, const uint64_t *numel,
+                                           uint32_t n_tensors, zero_dtype dt, uint64_t range_begin,
+                                           uint64_t count, void *dst, void *stream)
+{
+    if (dt != ZERO_F32 && dt != ZERO_F16 && dt != ZERO_BF16)
+        return fail(ZERO_EINVAL, "zero_bucket_flatten: bad dtype %d", (int)dt);
+    if (n_tensors > 0 && (!tensor_ptrs || !numel))
+        return fail(ZERO_EINVAL, "zero_bucket_flatten: NULL tensor table");
+    const uint64_t es = dt == ZERO_F32 ? 4 : 2;
+    uint64_t psi = 0;
+    for (uint32_t i = 0; i < n_tensors; ++i)
+        if (__builtin_add_overflow(psi, numel[i], &psi))
+            return fail(ZERO_EINVAL, "zero_bucket_flatten: total size overflows");
+    uint64_t range_end;
+    if (__builtin_add_overflow(range_begin, count, &range_end) || range_end > psi)
+        return fail(ZERO_EINVAL, "zero_bucket_flatten: range [%llu, +%llu) beyond %llu elements",
+                    (unsigned long long)range_begin, (unsigned long long)count,
+                    (unsigned long long)psi);
+    if (count == 0)
+        return ZERO_OK;
+    if (!dst)
+        return fail(ZERO_EINVAL, "zero_bucket_flatten: NULL dst");
+    if (!aligned(dst, es))
+        return fail(ZERO_EALIGN, "zero_bucket_flatten: dst not %llu-byte aligned",
+                    (unsigned long long)es);
+    if (count > UINT64_MAX / es)
+        return fail(ZERO_EINVAL, "zero_bucket_flatten: count too large");
+
+    // check every intersecting tensor before launching anything
+    uint64_t start = 0;
+    for (uint32_t i = 0; i < n_tensors; ++i) {
+        const uint64_t t_lo = start, t_hi = start + numel[i];
+        start = t_hi;
+        const uint64_t lo = t_lo > range_begin ? t_lo : range_begin;
+        const uint64_t hi = t_hi < range_end ? t_hi : range_end;
+        if (lo >= hi)
+            continue;
+        const char *src = (const char *)tensor_ptrs[i];
+        if (!src)
+            return fail(ZERO_EINVAL, "zero_bucket_flatten: NULL pointer for tensor %u", i);
+        if (!aligned(src, es))
+            return fail(ZERO_EALIGN, "zero_bucket_flatten: tensor %u not %llu-byte aligned", i,
+                        (unsigned long long)es);
+        if (overlap(src + (lo - t_lo) * es, (hi - lo) * es, dst, count * es))
+            return fail(ZERO_EINVAL, "zero_bucket_flatten: dst overlaps tensor %u", i);
+    }
+
+    FlatArgs a{};
+    a.dst = (char *)dst;
+    a.dst_phase = (uint32_t)(((uintptr_t)dst & 15u) / es);
+    start = 0;
+    for (uint32_t i = 0; i < n_tensors; ++i) {
+        const uint64_t t_lo = start, t_hi = start + numel[i];
+        start = t_hi;
+        const uint64_t lo = t_lo > range_begin ? t_lo : range_begin;
+        const uint64_t hi = t_hi < range_end ? t_hi : range_end;
+        if (lo >= hi)
+            continue;
+        const char *src = (const char *)tensor_ptrs[i];
+        // one segment: destination elements [lo - range_begin, hi - range_begin)
+        const uint32_t s = a.n_segs;
+        const uint64_t d_lo = lo - range_begin, d_hi = hi - range_begin;
+        const uint64_t V = 16 / es, ph = a.dst_phase;
+        const uint64_t c0 = (d_lo + ph + V - 1) / V, c1 = (d_hi + ph) / V;
+        const uint64_t full = c1 > c0 ? c1 - c0 : 0;
+        const uint64_t tiles = full ? (full + kFlatTileChunks - 1) / kFlatTileChunks : 1;
+        a.seg_lo[s] = d_lo;
+        a.seg_lo[s + 1] = d_hi;
+        a.src[s] = src + (lo - t_lo) * es;
+        a.tile_lo[s + 1] = a.tile_lo[s] + tiles;
+        a.n_segs = s + 1;
+        if (a.n_segs == kMaxSegs || hi == range_end) {
+            const zero_status st = es == 4 ? flatten_launch<4>(a, (hipStream_t)stream)
+                                           : flatten_launch<2>(a, (hipStream_t)stream);
+            if (st != ZERO_OK)
+                return st;
+            a.n_segs = 0;
+            a.tile_lo[0] = 0;
+        }
+    }
+    return ZERO_OK;
+}
+
+extern "C" zero_status zero_grad_stats_workspace(uint64_t n, size_t *bytes)
+{
+    if (!bytes)
+        return fail(ZERO_EINVAL, "zero_grad_stats_workspace: NULL output");
+    *bytes = (size_t)stats_blocks(n) * sizeof(Partial);
+    return ZERO_OK;
+}
+
+extern "C" zero_status zero_grad_stats(const void *grad, zero_dtype gdt, uint64_t n,
+                                       double inv_loss_scale, void *workspace, size_t ws_bytes,
+                                       zero_grad_stats_t *d_stats, void *stream)
+{
+    if (gdt != ZERO_F16 && gdt != ZERO_BF16)
+        return fail(ZERO_EINVAL, "zero_grad_stats: gradient dtype must be F16 or BF16");
+    if (!d_stats)
+        return fail(ZERO_EINVAL, "zero_grad_stats: NULL d_stats");
+    if (!(std::isfinite(inv_loss_scale) && inv_loss_scale > 0.0))
+        return fail(ZERO_EINVAL, "zero_grad_stats: inv_loss_scale must be finite and > 0");
+    if (n > 0 && !grad)
+        return fail(ZERO_EINVAL, "zero_grad_stats: NULL grad");
+    if (!workspace)
+        return fail(ZERO_EINVAL, "zero_grad_stats: NULL workspace");
+    const uint32_t blocks = stats_blocks(n);
+    if (ws_bytes < (size_t)blocks * sizeof(Partial))
+        return fail(ZERO_ENOSPC, "zero_grad_stats: workspace %zu bytes < %zu", ws_bytes,
+                    (size_t)blocks * sizeof(Partial));
+    if (!aligned(grad, 2) || !aligned(workspace, 16) || !aligned(d_stats, 8))
+        return fail(ZERO_EALIGN, "zero_grad_stats: misaligned pointer");
+    if (overlap(workspace, ws_bytes, d_stats, sizeof *d_stats) ||
+        overlap(workspace, ws_bytes, grad, 2 * n) || overlap(d_stats, sizeof *d_stats, grad, 2 * n))
+        return fail(ZERO_EINVAL, "zero_grad_stats: overlapping buffers");
+    hipStream_t s = (hipStream_t)stream;
+    const uint64_t ph = ((uintptr_t)grad & 15u) / 2;
+    uint64_t head = (8 - ph) % 8;
+    if (head > n) head = n;
+    const uint64_t nchunks = (n - head) / 8;
+    const uint64_t tail_beg = head + 8 * nchunks;
+    Partial *part = (Partial *)workspace;
+    const uint16_t *g = (const uint16_t *)grad;
+    if (gdt == ZERO_BF16)
+        hipLaunchKernelGGL(stats_pass1<true>, dim3(blocks), dim3(kBlock), 0, s, g, head, nchunks,
+                           tail_beg, n, part);
+    else
+        hipLaunchKernelGGL(stats_pass1<false>, dim3(blocks), dim3(kBlock), 0, s, g, head, nchunks,
+                           tail_beg, n, part);
+    zero_status st = launch_status("zero_grad_stats pass 1");
+    if (st != ZERO_OK)
+        return st;
+    hipLaunchKernelGGL(stats_pass2, dim3(1), dim3(kBlock), 0, s, (const Partial *)part, blocks,
+                       inv_loss_scale * inv_loss_scale, d_stats);
+    return launch_status("zero_grad_stats pass 2");
+}
+
+namespace {
+template <bool GB, bool PB>
+void launch_adam(const AdamArgs &a, uint32_t grid, hipStream_t s)
+{
+    const bool ga = a.g_phase == 0, pa = a.p_phase == 0;
+    if (ga && pa)
+        hipLaunchKernelGGL((adamw_stream<GB, PB, true, true>), dim3(grid), dim3(kBlock), 0, s, a);
+    else if (ga)
+        hipLaunchKernelGGL((adamw_stream<GB, PB, true, false>), dim3(grid), dim3(kBlock), 0, s, a);
+    else if (pa)
+        hipLaunchKernelGGL((adamw_stream<GB, PB, false, true>), dim3(grid), dim3(kBlock), 0, s, a);
+    else
+        hipLaunchKernelGGL((adamw_stream<GB, PB, false, false>), dim3(grid), dim3(kBlock), 0, s, a);
+}
+}  // namespace
+
+extern "C" zero_status zero_adam_step(const zero_adamw *hp, const void *grad, zero_dtype gdt,
+                                      float *master, float *exp_avg, float *exp_avg_sq,
+                                      void *param_out, zero_dtype pdt, uint64_t n,
+                                      const zero_grad_stats_t *d_stats, zero_adam_state_t *d_state,
+                                      void *stream)
+{
+    if (!hp)
+        return fail(ZERO_EINVAL, "zero_adam_step: NULL hyper-parameters");
+    if (!d_state)
+        return fail(ZERO_EINVAL, "zero_adam_step: NULL d_state");
+    if ((gdt != ZERO_F16 && gdt != ZERO_BF16) || (pdt != ZERO_F16 && pdt != ZERO_BF16))
+        return fail(ZERO_EINVAL, "zero_adam_step: grad and param dtypes must be F16 or BF16");
+    if (!(hp->lr >= 0.0 && std::isfinite(hp->lr)))
+        return fail(ZERO_EINVAL, "zero_adam_step: lr must be finite and >= 0");
+    if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0))
+        return fail(ZERO_EINVAL, "zero_adam_step: betas must be in [0, 1)");
+    if (!(hp->eps > 0.0 && std::isfinite(hp->eps)))
+        return fail(ZERO_EINVAL, "zero_adam_step: eps must be finite and > 0");
+    if (!(hp->weight_decay >= 0.0 && std::isfinite(hp->weight_decay)))
+        return fail(ZERO_EINVAL, "zero_adam_step: weight_decay must be finite and >= 0");
+    if (!(std::isfinite(hp->inv_loss_scale) && hp->inv_loss_scale > 0.0))
+        return fail(ZERO_EINVAL, "zero_adam_step: inv_loss_scale must be finite and > 0");
+    if (std::isnan(hp->max_grad_norm))
+        return fail(ZERO_EINVAL, "zero_adam_step: max_grad_norm is NaN");
+    if (n > 0 && (!grad || !master || !exp_avg || !exp_avg_sq || !param_out))
+        return fail(ZERO_EINVAL, "zero_adam_step: NULL array with n > 0");
+    if (n > UINT64_MAX / 4)
+        return fail(ZERO_EINVAL, "zero_adam_step: n too large");
+    if (!aligned(grad, 2) || !aligned(param_out, 2) || !aligned(master, 4) ||
+        !aligned(exp_avg, 4) || !aligned(exp_avg_sq, 4) || !aligned(d_state, 8) ||
+        !aligned(d_stats, 8))
+        return fail(ZERO_EALIGN, "zero_adam_step: misaligned pointer");
+    {
+        const void *buf[7] = {grad, master, exp_avg, exp_avg_sq, param_out, d_state, d_stats};
+        const uint64_t len[7] = {2 * n, 4 * n, 4 * n, 4 * n, 2 * n, sizeof(zero_adam_state_t),
+                                 d_stats ? sizeof(zero_grad_stats_t) : 0};
+        for (int i = 0; i < 7; ++i)
+            for (int j = i + 1; j < 7; ++j)
+                if (overlap(buf[i], len[i], buf[j], len[j]))
+                    return fail(ZERO_EINVAL, "zero_adam_step: buffers %d and %d overlap", i, j);
+    }
+    hipStream_t s = (hipStream_t)stream;
+    hipLaunchKernelGGL(adam_scalars, dim3(1), dim3(64), 0, s, *hp, d_stats, d_state);
+    zero_status st = launch_status("zero_adam_step scalars");
+    if (st != ZERO_OK || n == 0)
+        return st;
+
+    AdamArgs a{};
+    a.g = (const uint16_t *)grad;
+    a.master = master;
+    a.m = exp_avg;
+    a.v = exp_avg_sq;
+    a.p = (uint16_t *)param_out;
+    a.st = d_state;
+    a.n = n;
+    const uintptr_t fph = ((uintptr_t)master & 15u) / 4;
+    const bool same = fph == ((uintptr_t)exp_avg & 15u) / 4 && fph == ((uintptr_t)exp_avg_sq & 15u) / 4;
+    if (same) {
+        a.head = (4 - fph) % 4;
+        if (a.head > n) a.head = n;
+        a.nchunks = (n - a.head) / 8;
+    } else {  // fp32 arrays at different 16-byte phases: element by element
+        a.head = n;
+        a.nchunks = 0;
+    }
+    a.g_phase = (uint32_t)((((uintptr_t)grad & 15u) / 2 + a.head) % 8);
+    a.p_phase = (uint32_t)((((uintptr_t)param_out & 15u) / 2 + a.head) % 8);
+    if (a.nchunks == 0) {
+        a.g_phase = 0;
+        a.p_phase = 0;
+    }
+    const uint64_t work = a.nchunks ? a.nchunks : n;
+    const uint32_t grid = grid_for(work, (uint64_t)kBlock * kAdamUnroll, kAdamMaxBlocks);
+    const bool gb = gdt == ZERO_BF16, pb = pdt == ZERO_BF16;
+    if (gb && pb) launch_adam<true, true>(a, grid, s);
+    else if (gb) launch_adam<true, false>(a, grid, s);
+    else if (pb) launch_adam<false, true>(a, grid, s);
+    else launch_adam<false, false>(a, grid, s);
+    return launch_status("zero_adam_step");
+}
