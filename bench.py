@@ -149,6 +149,31 @@ def load_traffic(n_params: int):
     return d.get("bytes_per_launch")
 
 
+def copy_probe(steps: int):
+    """Plain device copies of a known size: the achievable streaming ceiling
+    (read + write, like the AdamW step) and the reference dispatch for
+    calibrating the HBM byte counters.  Prints one JSON line."""
+    import torch
+    n = 1 << 30  # fp32 elements: 4 GiB read + 4 GiB written per copy
+    src = torch.empty(n, dtype=torch.float32, device="cuda:0").normal_()
+    dst = torch.empty_like(src)
+    res = {}
+    for name, fn in (("copy_", lambda: dst.copy_(src)),
+                     ("mul_out", lambda: torch.mul(src, 1.0, out=dst))):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        res[name] = {"ms": ms, "GB/s": 2 * 4 * n / (ms * 1e-3) / 1e9,
+                     "bytes_read": 4 * n, "bytes_written": 4 * n}
+    print(json.dumps({"copy_probe": res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,11 +181,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="time plain device copies of a known size instead")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one data-parallel rank's shard on one GPU; runs on more "
               "than one GPU are not supported by this build", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe(args.steps)
+        return
 
     import torch
     dev = torch.device("cuda:0")

@@ -11,6 +11,11 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long-running CPU test")
 
 
+def pytest_sessionstart(session):
+    import util
+    util._reporter = session.config.pluginmanager.getplugin("terminalreporter")
+
+
 import pytest  # noqa: E402
 
 
@@ -19,6 +24,6 @@ def _announce_gpu_case(request):
     """Names each GPU case on the real stderr before it runs, so that a run
     that ends abruptly still says which case was running."""
     if request.node.get_closest_marker("gpu") is not None:
-        sys.__stderr__.write(f"\n[gpu case] {request.node.nodeid}\n")
-        sys.__stderr__.flush()
+        import util
+        util.progress(f"[gpu case] {request.node.nodeid}")
     yield

@@ -40,7 +40,12 @@ def _free():
 
 
 def _to_host16(t):
-    return t.cpu().numpy().view(NP16)
+    return t.view(torch.int16).cpu().numpy().view(NP16)
+
+
+def _dev16(bits, like):
+    """A one-element device tensor holding the 16-bit pattern `bits`."""
+    return torch.from_numpy(np.array([bits], NP16).view(np.int16)).view(like.dtype).to(dev())
 
 
 def _sample_indices(cfg, begin, end, n_random, seed, bucket=None):
@@ -190,7 +195,7 @@ def test_workload5_shard_skip_full():
         del host, sub
         if k == inj_step:
             for i, bits in inj:
-                r.g[i] = torch.tensor(bits, dtype=torch.int16).view(r.g.dtype).to(dev())
+                r.g[i:i + 1] = _dev16(bits, r.g)
                 g_ref[i] = bits
         assert np.array_equal(_to_host16(r.g), g_ref), k
         th0, m0, v0 = (a.cpu().numpy().copy() for a in (r.master, r.m, r.v))
@@ -237,7 +242,7 @@ def test_workload5_single_nan_at_last_element():
     r = Rank(cfg, p_phase=oracle.partition(cfg.psi, cfg.nd, cfg.rank)[0] % 8)
     gen.device_fill_normal_(r.master, cfg.master_seed(), cfg.master_sigma)
     r.gather(_w5_grads(cfg, r, 0))
-    r.g[r.n - 1] = torch.tensor(gen.F16_NAN, dtype=torch.int16).view(r.g.dtype).to(dev())
+    r.g[r.n - 1:] = _dev16(gen.F16_NAN, r.g)
     before = [a.clone() for a in (r.master, r.m, r.v, r.p_raw)]
     r.stats_and_step()
     torch.cuda.synchronize()

@@ -118,7 +118,14 @@ class FreeRunScales:
         return out
 
 
+_reporter = None  # pytest's terminal reporter, set by conftest
+
+
 def progress(msg):
-    import sys
-    sys.__stderr__.write(f"    [progress] {msg}\n")
-    sys.__stderr__.flush()
+    """A progress line that reaches the terminal even while output is captured."""
+    line = f"    [progress] {msg}"
+    if _reporter is not None:
+        _reporter.write_line(line)
+        _reporter._tw.flush()
+    else:
+        print(line, flush=True)

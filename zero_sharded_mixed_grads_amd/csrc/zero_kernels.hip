@@ -25,9 +25,9 @@
 // No scalar-cache writes, no float atomics: results are bit-reproducible.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
-#include <vector>
 
 #include "zero_internal.h"
 
@@ -36,6 +36,54 @@ using zero::fail;
 namespace {
 
 constexpr int kBlock = 256;  // 4 waves of 64 lanes
+
+// Tuning knobs of the streaming kernels (compile-time).
+#ifndef ZERO_ADAM_UNROLL
+#define ZERO_ADAM_UNROLL 2   // 8-element chunks per lane kept in flight
+#endif
+#ifndef ZERO_NT_STORE
+#define ZERO_NT_STORE 0      // 1: non-temporal hint on the AdamW body stores
+#endif
+#ifndef ZERO_NT_LOAD
+#define ZERO_NT_LOAD 0       // 1: non-temporal hint on the AdamW body loads
+#endif
+#ifndef ZERO_BLOCKS_PER_CU
+#define ZERO_BLOCKS_PER_CU 0 // 0: as many as the occupancy calculator allows
+#endif
+
+// Native vector types behind HIP's vector structs (the non-temporal builtins
+// take scalars or native vectors only).
+template <typename T> struct native { using type = T; };
+template <> struct native<uint4> { using type = unsigned int __attribute__((ext_vector_type(4))); };
+template <> struct native<uint2> { using type = unsigned int __attribute__((ext_vector_type(2))); };
+template <> struct native<float4> { using type = float __attribute__((ext_vector_type(4))); };
+
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T *p)
+{
+#if ZERO_NT_LOAD
+    using N = typename native<T>::type;
+    const N x = __builtin_nontemporal_load(reinterpret_cast<const N *>(p));
+    T v;
+    __builtin_memcpy(&v, &x, sizeof v);
+    return v;
+#else
+    return *p;
+#endif
+}
+
+template <typename T>
+__device__ __forceinline__ void st_stream(T *p, const T &v)
+{
+#if ZERO_NT_STORE
+    using N = typename native<T>::type;
+    N x;
+    __builtin_memcpy(&x, &v, sizeof v);
+    __builtin_nontemporal_store(x, reinterpret_cast<N *>(p));
+#else
+    *p = v;
+#endif
+}
 
 // ------------------------------------------------------------ 16-bit helpers
 template <bool BF16>
@@ -119,17 +167,19 @@ __device__ __forceinline__ void store_run(uint16_t *line, const uint32_t *h)
     if constexpr (COUNT <= 0) {
         return;
     } else if constexpr ((SLOT & 1) || COUNT == 1) {
-        line[SLOT] = (uint16_t)h[0];
+        st_stream(line + SLOT, (uint16_t)h[0]);
         store_run<SLOT + 1, COUNT - 1>(line, h + 1);
     } else if constexpr (SLOT % 8 == 0 && COUNT >= 8) {
-        *reinterpret_cast<uint4 *>(line + SLOT) =
-            make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16);
+        st_stream(reinterpret_cast<uint4 *>(line + SLOT),
+                  make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16,
+                             h[6] | h[7] << 16));
         store_run<SLOT + 8, COUNT - 8>(line, h + 8);
     } else if constexpr (SLOT % 4 == 0 && COUNT >= 4) {
-        *reinterpret_cast<uint2 *>(line + SLOT) = make_uint2(h[0] | h[1] << 16, h[2] | h[3] << 16);
+        st_stream(reinterpret_cast<uint2 *>(line + SLOT),
+                  make_uint2(h[0] | h[1] << 16, h[2] | h[3] << 16));
         store_run<SLOT + 4, COUNT - 4>(line, h + 4);
     } else {
-        *reinterpret_cast<uint32_t *>(line + SLOT) = h[0] | h[1] << 16;
+        st_stream(reinterpret_cast<uint32_t *>(line + SLOT), h[0] | h[1] << 16);
         store_run<SLOT + 2, COUNT - 2>(line, h + 2);
     }
 }
@@ -176,7 +226,6 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t x)
 constexpr int kMaxSegs = 96;         // segments per launch (kernel-argument table)
 constexpr int kFlatChunksPerThread = 4;
 constexpr uint64_t kFlatTileChunks = (uint64_t)kBlock * kFlatChunksPerThread;
-constexpr int kFlatMaxBlocks = 2048;
 
 struct FlatArgs {
     char *dst;                     // element 0 of the destination range
@@ -476,8 +525,7 @@ __device__ __forceinline__ void adamw_elem(const Coeffs &k, float graw, float &t
     v = v1;
 }
 
-constexpr int kAdamUnroll = 2;
-constexpr int kAdamMaxBlocks = 2048;
+constexpr int kAdamUnroll = ZERO_ADAM_UNROLL;
 
 template <bool GBF16, bool PBF16, bool G_ALIGNED, bool P_ALIGNED>
 __global__ void __launch_bounds__(kBlock) adamw_stream(AdamArgs a)
@@ -506,14 +554,14 @@ __global__ void __launch_bounds__(kBlock) adamw_stream(AdamArgs a)
             const uint64_t c = base + j * stride;
             if (c < a.nchunks) {
                 if constexpr (G_ALIGNED) {
-                    gw[j] = gl[c];
+                    gw[j] = ld_stream(gl + c);
                 } else {
-                    const uint4 lo = gl[c], hi = gl[c + 1];
+                    const uint4 lo = ld_stream(gl + c), hi = ld_stream(gl + c + 1);
                     gw[j] = shift_lines_rt(lo, hi, gsb);
                 }
-                th[j][0] = th4[2 * c]; th[j][1] = th4[2 * c + 1];
-                mm[j][0] = m4[2 * c];  mm[j][1] = m4[2 * c + 1];
-                vv[j][0] = v4[2 * c];  vv[j][1] = v4[2 * c + 1];
+                th[j][0] = ld_stream(th4 + 2 * c); th[j][1] = ld_stream(th4 + 2 * c + 1);
+                mm[j][0] = ld_stream(m4 + 2 * c);  mm[j][1] = ld_stream(m4 + 2 * c + 1);
+                vv[j][0] = ld_stream(v4 + 2 * c);  vv[j][1] = ld_stream(v4 + 2 * c + 1);
             }
         }
 #pragma unroll
@@ -532,9 +580,9 @@ __global__ void __launch_bounds__(kBlock) adamw_stream(AdamArgs a)
                     adamw_elem(k, graw, t[e], mv[e], vw[e]);
                     ph[e] = from_f32<PBF16>(t[e]);
                 }
-                th4[2 * c] = th[j][0]; th4[2 * c + 1] = th[j][1];
-                m4[2 * c] = mm[j][0];  m4[2 * c + 1] = mm[j][1];
-                v4[2 * c] = vv[j][0];  v4[2 * c + 1] = vv[j][1];
+                st_stream(th4 + 2 * c, th[j][0]); st_stream(th4 + 2 * c + 1, th[j][1]);
+                st_stream(m4 + 2 * c, mm[j][0]);  st_stream(m4 + 2 * c + 1, mm[j][1]);
+                st_stream(v4 + 2 * c, vv[j][0]);  st_stream(v4 + 2 * c + 1, vv[j][1]);
                 if constexpr (P_ALIGNED)
                     store_run<0, 8>(pl + 8 * c, ph);
                 else
@@ -573,6 +621,33 @@ zero_status launch_status(const char *what)
     return ZERO_OK;
 }
 
+// Blocks of `kernel` that the current device keeps resident at once (CUs x
+// blocks per CU from the occupancy calculator), cached per device.
+template <typename K>
+uint32_t resident_blocks(K kernel)
+{
+    constexpr int kMaxDev = 64;
+    static std::atomic<uint32_t> cache[kMaxDev];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev)
+        return 1024;
+    uint32_t v = cache[dev].load(std::memory_order_relaxed);
+    if (v)
+        return v;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    if (ZERO_BLOCKS_PER_CU > 0)
+        per_cu = ZERO_BLOCKS_PER_CU;
+    else if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0) !=
+                 hipSuccess || per_cu <= 0)
+        per_cu = 4;
+    v = (uint32_t)(cus * per_cu);
+    cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
 inline uint32_t grid_for(uint64_t work_items, uint64_t per_block, uint32_t max_blocks)
 {
     uint64_t b = (work_items + per_block - 1) / per_block;
@@ -584,7 +659,7 @@ inline uint32_t grid_for(uint64_t work_items, uint64_t per_block, uint32_t max_b
 template <int ES>
 zero_status flatten_launch(FlatArgs &a, hipStream_t stream)
 {
-    const uint32_t grid = grid_for(a.tile_lo[a.n_segs], 1, kFlatMaxBlocks);
+    const uint32_t grid = grid_for(a.tile_lo[a.n_segs], 1, resident_blocks(flatten_segments<ES>));
     hipLaunchKernelGGL(flatten_segments<ES>, dim3(grid), dim3(kBlock), 0, stream, a);
     return launch_status("zero_bucket_flatten");
 }
@@ -729,18 +804,22 @@ extern "C" zero_status zero_grad_stats(const void *grad, zero_dtype gdt, uint64_
 }
 
 namespace {
+template <bool GB, bool PB, bool GA, bool PA>
+void launch_adam_variant(const AdamArgs &a, uint64_t work, hipStream_t s)
+{
+    auto kernel = adamw_stream<GB, PB, GA, PA>;
+    const uint32_t grid = grid_for(work, (uint64_t)kBlock * kAdamUnroll, resident_blocks(kernel));
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), 0, s, a);
+}
+
 template <bool GB, bool PB>
-void launch_adam(const AdamArgs &a, uint32_t grid, hipStream_t s)
+void launch_adam(const AdamArgs &a, uint64_t work, hipStream_t s)
 {
     const bool ga = a.g_phase == 0, pa = a.p_phase == 0;
-    if (ga && pa)
-        hipLaunchKernelGGL((adamw_stream<GB, PB, true, true>), dim3(grid), dim3(kBlock), 0, s, a);
-    else if (ga)
-        hipLaunchKernelGGL((adamw_stream<GB, PB, true, false>), dim3(grid), dim3(kBlock), 0, s, a);
-    else if (pa)
-        hipLaunchKernelGGL((adamw_stream<GB, PB, false, true>), dim3(grid), dim3(kBlock), 0, s, a);
-    else
-        hipLaunchKernelGGL((adamw_stream<GB, PB, false, false>), dim3(grid), dim3(kBlock), 0, s, a);
+    if (ga && pa) launch_adam_variant<GB, PB, true, true>(a, work, s);
+    else if (ga) launch_adam_variant<GB, PB, true, false>(a, work, s);
+    else if (pa) launch_adam_variant<GB, PB, false, true>(a, work, s);
+    else launch_adam_variant<GB, PB, false, false>(a, work, s);
 }
 }  // namespace
 
@@ -816,11 +895,10 @@ extern "C" zero_status zero_adam_step(const zero_adamw *hp, const void *grad, ze
         a.p_phase = 0;
     }
     const uint64_t work = a.nchunks ? a.nchunks : n;
-    const uint32_t grid = grid_for(work, (uint64_t)kBlock * kAdamUnroll, kAdamMaxBlocks);
     const bool gb = gdt == ZERO_BF16, pb = pdt == ZERO_BF16;
-    if (gb && pb) launch_adam<true, true>(a, grid, s);
-    else if (gb) launch_adam<true, false>(a, grid, s);
-    else if (pb) launch_adam<false, true>(a, grid, s);
-    else launch_adam<false, false>(a, grid, s);
+    if (gb && pb) launch_adam<true, true>(a, work, s);
+    else if (gb) launch_adam<true, false>(a, work, s);
+    else if (pb) launch_adam<false, true>(a, work, s);
+    else launch_adam<false, false>(a, work, s);
     return launch_status("zero_adam_step");
 }
