@@ -157,9 +157,14 @@ def copy_probe(steps: int):
     n = 1 << 30  # fp32 elements: 4 GiB read + 4 GiB written per copy
     src = torch.empty(n, dtype=torch.float32, device="cuda:0").normal_()
     dst = torch.empty_like(src)
+    import zero_sharded_mixed_grads_amd as z
     res = {}
     for name, fn in (("copy_", lambda: dst.copy_(src)),
-                     ("mul_out", lambda: torch.mul(src, 1.0, out=dst))):
+                     ("mul_out", lambda: torch.mul(src, 1.0, out=dst)),
+                     # the library's own gather of one aligned fp32 tensor: a plain copy
+                     # with the same 16-byte load/store pattern as the path's kernels
+                     ("zero_bucket_flatten", lambda: z.zero_bucket_flatten([src], [n], "f32", 0,
+                                                                           n, dst))):
         fn()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -213,7 +218,16 @@ def main():
     ms = np.array([[a.elapsed_time(b) for a, b in zip(e[:-1], e[1:])] for e in evs])
     flat_ms, stats_ms, adam_ms = ms.mean(axis=0)
     log(f"[bench] timed {args.steps} steps in {wall:.3f}s; per step flatten {flat_ms:.3f} ms, "
-        f"stats {stats_ms:.3f} ms, adam {adam_ms:.3f} ms")
+        f"stats {stats_ms:.3f} ms, adam {adam_ms:.3f} ms "
+        f"(adam min {ms[:, 2].min():.3f} max {ms[:, 2].max():.3f})")
+    # every step must have been a real update: the device step counter counts them
+    st = w.z.read_adam_state(w.state)
+    gs = w.z.read_grad_stats(w.stats)
+    taken = args.warmup + args.steps
+    if st.step != taken or gs.overflow:
+        print(f"bench: {taken - st.step} of {taken} steps were skipped (overflow={gs.overflow}); "
+              "the measurement is invalid", file=sys.stderr)
+        sys.exit(3)
 
     n = w.n
     step_ms = wall * 1e3 / args.steps
@@ -240,7 +254,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": adam_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": adam_gbs / HBM_PEAK_GBS, "traffic": traffic},
         "kernels": {
-            "adam_step": {"ms": adam_ms, "params_per_s": n / (adam_ms * 1e-3),
+            "adam_step": {"ms": adam_ms, "ms_min": float(ms[:, 2].min()),
+                          "ms_max": float(ms[:, 2].max()), "params_per_s": n / (adam_ms * 1e-3),
                           "GB/s": adam_gbs, "bytes_per_param": ADAM_BYTES_PER_PARAM},
             "grad_stats": {"ms": stats_ms,
                            "GB/s": STATS_BYTES_PER_PARAM * n / (stats_ms * 1e-3) / 1e9,
@@ -251,6 +266,8 @@ def main():
         },
         "step_bytes_per_param": ADAM_BYTES_PER_PARAM + STATS_BYTES_PER_PARAM +
                                 FLATTEN_BYTES_PER_PARAM,
+        "checks": {"device_steps_taken": int(st.step), "overflow": int(gs.overflow),
+                   "sq_norm": gs.sq_norm, "clip_coef": st.coef},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")

@@ -145,8 +145,9 @@ zero_status zero_grad_stats_workspace(uint64_t n, size_t *bytes);
  * n 16-bit gradients (gdt F16 or BF16, stored multiplied by the loss
  * scale), and writes *d_stats (device memory) with the overflow flag (any
  * non-finite element) and the squared L2 norm of g * inv_loss_scale,
- * accumulated in fp64 in a fixed order (bit-reproducible for a given n).
- * sq_norm is unspecified when overflow is set.  n == 0 writes {0, 0}.
+ * accumulated in fp64 in a fixed order (bit-reproducible for a given n and
+ * 16-byte phase of grad).  sq_norm is unspecified when overflow is set.
+ * n == 0 writes {0, 0}.
  * Multi-rank callers sum sq_norm and take the max of overflow across ranks
  * on the same stream before zero_adam_step.
  * workspace: device memory of at least zero_grad_stats_workspace(n) bytes,

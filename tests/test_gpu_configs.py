@@ -27,7 +27,7 @@ import torch
 import oracle
 import zero_sharded_mixed_grads_amd as z
 from synth import CONFIGS, gen
-from util import FreeRunScales, check_adam_one_step, dev, progress, ulp16_dist
+from util import FreeRunScales, check_adam_one_step, check_params16, dev, progress
 
 pytestmark = pytest.mark.gpu
 
@@ -152,15 +152,15 @@ def test_workload1_tiny_full():
         oracle.adamw_(s1, g_ref, cfg.dtype, th1, m1, v1, p1, cfg.dtype)
         th_g, m_g, v_g = (a.cpu().numpy() for a in (r.master, r.m, r.v))
         p_g = _to_host16(r.p)
-        check_adam_one_step(cfg.hp, s1, gv, th0, m0, v0, th_g, m_g, v_g, th1, m1, v1,
-                            label=f"step {k}")
-        assert ulp16_dist(p_g, p1).max() <= 1
+        e1 = check_adam_one_step(cfg.hp, s1, gv, th0, m0, v0, th_g, m_g, v_g, th1, m1, v1,
+                                 label=f"step {k}")
+        check_params16(p_g, th_g, th1, e1.pop("master_scale"), 1e-6, cfg.dtype, f"step {k}")
         # free-running
         s = oracle.step_scalars(cfg.hp, True, sq, ov, k)
         oracle.adamw_(s, g_ref, cfg.dtype, th_o, m_o, v_o, p_o, cfg.dtype)
         scales.update(s, gv, m_o, v_o)
         errs = scales.check(th_g, m_g, v_g, th_o, m_o, v_o, label=f"step {k}")
-        assert ulp16_dist(p_g, p_o).max() <= 1
+        check_params16(p_g, th_g, th_o, errs.pop("master_scale"), 1e-5, cfg.dtype, f"step {k}")
         worst = {key: max(worst.get(key, 0), val) for key, val in errs.items()}
     assert z.read_adam_state(r.state).step == cfg.steps
     progress(f"workload 1: worst free-running error / scale {worst}")
@@ -221,16 +221,18 @@ def test_workload5_shard_skip_full():
         assert s1.coef < 1.0  # clipping is active on this workload
         th1, m1, v1, p1 = th0.copy(), m0.copy(), v0.copy(), np.zeros(n, NP16)
         oracle.adamw_(s1, g_ref, cfg.dtype, th1, m1, v1, p1, cfg.dtype)
-        check_adam_one_step(cfg.hp, s1, gv, th0, m0, v0, th_g, m_g, v_g, th1, m1, v1,
-                            label=f"step {k}")
-        assert ulp16_dist(p_g, p1).max() <= 1
-        progress(f"workload 5 step {k}: sq {st.sq_norm:.6e} (oracle {sq:.6e})")
+        e1 = check_adam_one_step(cfg.hp, s1, gv, th0, m0, v0, th_g, m_g, v_g, th1, m1, v1,
+                                 label=f"step {k}")
+        check_params16(p_g, th_g, th1, e1.pop("master_scale"), 1e-6, cfg.dtype, f"step {k}")
         del th1, m1, v1, p1
         s = oracle.step_scalars(cfg.hp, True, sq, ov, t_expect - 1)
         oracle.adamw_(s, g_ref, cfg.dtype, th_o, m_o, v_o, p_o, cfg.dtype)
         scales.update(s, gv, m_o, v_o)
-        scales.check(th_g, m_g, v_g, th_o, m_o, v_o, label=f"step {k}")
-        assert ulp16_dist(p_g, p_o).max() <= 1
+        e2 = scales.check(th_g, m_g, v_g, th_o, m_o, v_o, label=f"step {k}")
+        far = check_params16(p_g, th_g, th_o, e2.pop("master_scale"), 1e-5, cfg.dtype,
+                             f"step {k}")
+        progress(f"workload 5 step {k}: sq {st.sq_norm:.9e} (oracle {sq:.9e}) one-step {e1} "
+                 f"free {e2} params beyond 1 ulp: {far}")
         del grads
     assert t_expect == cfg.steps - 1
     # the 16-bit lead pad before the phase-faithful slice was never written
@@ -306,14 +308,17 @@ def _run_sampled(cfg, r, idx, fill_grads, label):
         p_g = _to_host16(r.p[idx_t])
         e1 = check_adam_one_step(cfg.hp, s1, gv, th0, m0, v0, th_g, m_g, v_g, th1, m1, v1,
                                  label=f"{label} step {k}")
-        assert ulp16_dist(p_g, p1).max() <= 1
+        f1 = check_params16(p_g, th_g, th1, e1.pop("master_scale"), 1e-6, cfg.dtype,
+                            f"{label} step {k}")
         s = oracle.step_scalars(cfg.hp, True, sq, ov, k)
         oracle.adamw_(s, g_s, cfg.dtype, th_o, m_o, v_o, p_o, cfg.dtype)
         scales.update(s, gv, m_o, v_o)
         e2 = scales.check(th_g, m_g, v_g, th_o, m_o, v_o, label=f"{label} step {k}")
-        assert ulp16_dist(p_g, p_o).max() <= 1
+        f2 = check_params16(p_g, th_g, th_o, e2.pop("master_scale"), 1e-5, cfg.dtype,
+                            f"{label} step {k}")
         progress(f"{label} step {k}: sq {st.sq_norm:.9e} rel.err {abs(st.sq_norm - sq) / sq:.1e} "
-                 f"coef {s.coef:.6f} one-step {e1} free {e2}")
+                 f"coef {s.coef:.6f} one-step {e1} free {e2} params beyond 1 ulp: {f1}/{f2} "
+                 f"of {idx.size}")
     assert z.read_adam_state(r.state).step == cfg.steps
 
 

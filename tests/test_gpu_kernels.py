@@ -13,7 +13,7 @@ import torch
 import oracle
 import zero_sharded_mixed_grads_amd as z
 from synth import AdamW, gen
-from util import Guarded, check_adam_one_step, dev, ulp16_dist
+from util import Guarded, check_adam_one_step, check_params16, dev
 
 pytestmark = pytest.mark.gpu
 
@@ -189,9 +189,9 @@ def test_adam_one_step_dtypes_sizes(gdt, pdt, n):
     c = _adam_case(n, gdt, pdt, 0, 0, (0, 0, 0), hp, seed=n)
     st = z.read_grad_stats(c["stats"])
     s, th, m, v, p = _oracle_step(c, hp, gdt, pdt, True, st.sq_norm, st.overflow)
-    check_adam_one_step(hp, s, oracle.value16(c["gb"], gdt), c["th0"], c["m0"], c["v0"],
-                        c["th"].host(), c["m"].host(), c["v"].host(), th, m, v)
-    assert ulp16_dist(c["p"].host(), p).max() <= 1
+    e = check_adam_one_step(hp, s, oracle.value16(c["gb"], gdt), c["th0"], c["m0"],
+                            c["v0"], c["th"].host(), c["m"].host(), c["v"].host(), th, m, v)
+    check_params16(c["p"].host(), c["th"].host(), th, e["master_scale"], 1e-6, pdt)
     sa = z.read_adam_state(c["state"])
     assert sa.step == 1 and sa.skip == 0 and abs(sa.coef - s.coef) <= 1e-12
     for b in ("g", "th", "m", "v", "p"):
@@ -206,9 +206,9 @@ def test_adam_16bit_phases(g_phase, p_phase):
     c = _adam_case(n, "f16", "f16", g_phase, p_phase, (1, 1, 1), hp, seed=g_phase * 8 + p_phase)
     st = z.read_grad_stats(c["stats"])
     s, th, m, v, p = _oracle_step(c, hp, "f16", "f16", True, st.sq_norm, st.overflow)
-    check_adam_one_step(hp, s, oracle.value16(c["gb"], "f16"), c["th0"], c["m0"], c["v0"],
-                        c["th"].host(), c["m"].host(), c["v"].host(), th, m, v)
-    assert ulp16_dist(c["p"].host(), p).max() <= 1
+    e = check_adam_one_step(hp, s, oracle.value16(c["gb"], "f16"), c["th0"], c["m0"],
+                            c["v0"], c["th"].host(), c["m"].host(), c["v"].host(), th, m, v)
+    check_params16(c["p"].host(), c["th"].host(), th, e["master_scale"], 1e-6, "f16")
     for b in ("g", "th", "m", "v", "p"):
         assert c[b].canaries_intact(), b
 
@@ -221,9 +221,9 @@ def test_adam_fp32_phases_and_fallback(f_phases):
         c = _adam_case(n, "bf16", "bf16", 3, 6, f_phases, hp, seed=n + sum(f_phases))
         st = z.read_grad_stats(c["stats"])
         s, th, m, v, p = _oracle_step(c, hp, "bf16", "bf16", True, st.sq_norm, st.overflow)
-        check_adam_one_step(hp, s, oracle.value16(c["gb"], "bf16"), c["th0"], c["m0"], c["v0"],
-                            c["th"].host(), c["m"].host(), c["v"].host(), th, m, v)
-        assert ulp16_dist(c["p"].host(), p).max() <= 1
+        e = check_adam_one_step(hp, s, oracle.value16(c["gb"], "bf16"), c["th0"], c["m0"],
+                                c["v0"], c["th"].host(), c["m"].host(), c["v"].host(), th, m, v)
+        check_params16(c["p"].host(), c["th"].host(), th, e["master_scale"], 1e-6, "bf16")
         for b in ("g", "th", "m", "v", "p"):
             assert c[b].canaries_intact(), b
 
@@ -293,3 +293,45 @@ def test_adam_step_counter_and_determinism():
         assert z.read_adam_state(state).step == 3
     for a, b in zip(*outs):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_param_rounding_every_tie(dtype):
+    """With lr = wd = 0 the master is unchanged, so the param must be the
+    round-to-nearest-even of the given fp32 master.  Inputs: every finite
+    16-bit value, every exact midpoint between neighbours (ties), +-1 fp32
+    ulp around each midpoint, and values past the largest finite one.
+    Reference: numpy (binary16) and torch (bfloat16) rounding."""
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    if dtype == "f16":
+        v = b.view(np.float16).astype(np.float32)
+    else:
+        v = (b.astype(np.uint32) << 16).view(np.float32)
+    v = v[np.isfinite(v)]
+    pos = np.sort(v[v >= 0].astype(np.float64))
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    assert np.array_equal(mids.astype(np.float64), (pos[:-1] + pos[1:]) / 2)  # exact ties
+    x = np.concatenate([v, mids, -mids, np.nextafter(mids, np.float32(np.inf)),
+                        np.nextafter(mids, np.float32(0)),
+                        np.float32([65519.99, 65520.0, 1e5, 3.4e38, -3.4e38])])
+    n = x.size
+    hp = AdamW(lr=0.0, weight_decay=0.0)
+    g = Guarded(n, np.uint16, phase=3, init=np.zeros(n, np.uint16))
+    th = Guarded(n, np.float32, phase=0, init=x)
+    m = Guarded(n, np.float32, phase=0, init=np.zeros(n, np.float32))
+    v_ = Guarded(n, np.float32, phase=0, init=np.zeros(n, np.float32))
+    p = Guarded(n, np.uint16, phase=5)
+    state = z.new_adam_state(dev())
+    z.zero_adam_step(z.adamw(**hp.__dict__), g.ptr(), dtype, th.ptr(), m.ptr(), v_.ptr(), p.ptr(),
+                     dtype, n, None, state)
+    torch.cuda.synchronize()
+    # master unchanged in value (IEEE arithmetic maps -0 - 0*(-0) to +0)
+    assert np.array_equal(th.host(), x)
+    xr = x + np.float32(0.0)  # the same -0 -> +0 mapping for the reference
+    with np.errstate(over="ignore"):
+        ref = (xr.astype(np.float16).view(np.uint16) if dtype == "f16" else
+               torch.from_numpy(xr).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    got = p.host()
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(float(x[i]), hex(got[i]), hex(ref[i])) for i in bad[:5]]
+    assert p.canaries_intact()

@@ -53,6 +53,37 @@ def ulp16_dist(a, b):
     return np.abs(ordered16(a) - ordered16(b))
 
 
+def check_params16(p, th, th_ref, th_scale, tol, dtype, label=""):
+    """16-bit params: (1) exactly the round-to-nearest-even of the GPU's own
+    fp32 master; (2) within 1 ulp of the oracle's param, or else inside the
+    rounding of the master's tolerance interval [th_ref -+ tol*scale].  The
+    second clause matters only where the master cancels to near zero: bf16
+    has no subnormal floor there, so a master error that is tiny against the
+    update's scale can span several ulps of the tiny value."""
+    import oracle
+    exact = oracle.bits16(np.asarray(th, np.float32), dtype)
+    if not np.array_equal(p, exact):
+        i = int(np.argmax(p != exact))
+        raise AssertionError(f"{label} param[{i}] {p[i]:#06x} is not RNE of its master "
+                             f"{th[i]!r} ({exact[i]:#06x})")
+    p_ref = oracle.bits16(np.asarray(th_ref, np.float32), dtype)
+    d = ulp16_dist(p, p_ref)
+    far = d > 1
+    if far.any():
+        dlt = tol * th_scale[far]
+        lo = oracle.bits16(np.nextafter((th_ref[far] - dlt).astype(np.float32), np.float32(-np.inf)),
+                           dtype)
+        hi = oracle.bits16(np.nextafter((th_ref[far] + dlt).astype(np.float32), np.float32(np.inf)),
+                           dtype)
+        q = ordered16(p[far])
+        inside = (q >= ordered16(lo)) & (q <= ordered16(hi))
+        if not inside.all():
+            i = int(np.nonzero(far)[0][np.argmax(~inside)])
+            raise AssertionError(f"{label} param[{i}] {p[i]:#06x} vs oracle {p_ref[i]:#06x} "
+                                 f"(master {th[i]!r}, oracle master {th_ref[i]!r})")
+    return int(far.sum())
+
+
 def check_adam_one_step(hp, s, g_val, th0, m0, v0, th, m, v, th_ref, m_ref, v_ref,
                         tol=1e-6, label=""):
     """Per-element bounds of one step from a common state (th0, m0, v0):
@@ -79,6 +110,7 @@ def check_adam_one_step(hp, s, g_val, th0, m0, v0, th, m, v, th_ref, m_ref, v_re
                                  f"err {d[i]:.3e} bound {tol * sc[i]:.3e}")
         with np.errstate(divide="ignore", invalid="ignore"):
             errs[name] = float(np.nanmax(np.where(sc > 0, d / sc, 0.0))) if d.size else 0.0
+    errs["master_scale"] = th_scale
     return errs
 
 
@@ -115,6 +147,7 @@ class FreeRunScales:
                                      f"ref {r[i]!r} err {d[i]:.3e} bound {tol * sc[i]:.3e}")
             with np.errstate(divide="ignore", invalid="ignore"):
                 out[name] = float(np.nanmax(np.where(sc > 0, d / sc, 0.0))) if d.size else 0.0
+        out["master_scale"] = np.maximum(self.T, np.abs(th_ref))
         return out
 
 

@@ -35,7 +35,10 @@ using zero::fail;
 
 namespace {
 
-constexpr int kBlock = 256;  // 4 waves of 64 lanes
+#ifndef ZERO_BLOCK
+#define ZERO_BLOCK 256
+#endif
+constexpr int kBlock = ZERO_BLOCK;  // threads per block (waves of 64 lanes)
 
 // Tuning knobs of the streaming kernels (compile-time).
 #ifndef ZERO_ADAM_UNROLL
@@ -49,6 +52,23 @@ constexpr int kBlock = 256;  // 4 waves of 64 lanes
 #endif
 #ifndef ZERO_BLOCKS_PER_CU
 #define ZERO_BLOCKS_PER_CU 0 // 0: as many as the occupancy calculator allows
+#endif
+#ifndef ZERO_FAST_SQRT_RCP
+#define ZERO_FAST_SQRT_RCP 0 // 1: hardware v_sqrt_f32 / v_rcp_f32 (about 1 ulp each)
+#endif
+#ifndef ZERO_ADAM_MAPPING
+#define ZERO_ADAM_MAPPING 2  // 0: persistent grid-stride chunks; 1: persistent grid-stride
+                             // over contiguous tiles; 2: one contiguous tile per block
+#endif
+#ifndef ZERO_XCD_ORDER
+#define ZERO_XCD_ORDER 1     // 1 (with one tile per block): block i runs on XCD i % 8, so
+                             // tiles are renumbered to give each XCD a contiguous eighth
+#endif
+#ifndef ZERO_FLAT_CPT
+#define ZERO_FLAT_CPT 1      // 16-byte lines per thread in a flatten tile
+#endif
+#ifndef ZERO_FLAT_ONESHOT
+#define ZERO_FLAT_ONESHOT 1  // 1: one flatten tile per block instead of a resident grid
 #endif
 
 // Native vector types behind HIP's vector structs (the non-temporal builtins
@@ -119,6 +139,11 @@ __device__ __forceinline__ uint32_t from_f32(float x)
         u += 0x7fffu + ((u >> 16) & 1u);
         return u >> 16;
     } else {
+        // The barrier makes x an opaque, already rounded fp32 value: without it
+        // the backend folds "fma then convert" into v_fma_mixlo_f16, which
+        // rounds the exact fma result to f16 once instead of rounding the
+        // stored fp32 master, and differs from it at fp32 ties.
+        asm volatile("" : "+v"(x));
         _Float16 h = (_Float16)x;  // v_cvt_f16_f32, round-to-nearest-even mode
         uint16_t b;
         __builtin_memcpy(&b, &h, 2);
@@ -215,16 +240,9 @@ __device__ __forceinline__ double wave_sum(double x)
     return x;
 }
 
-__device__ __forceinline__ uint32_t wave_or(uint32_t x)
-{
-    for (int o = 32; o > 0; o >>= 1)
-        x |= __shfl_xor(x, o, 64);
-    return x;
-}
-
 // ================================================================ flatten
 constexpr int kMaxSegs = 96;         // segments per launch (kernel-argument table)
-constexpr int kFlatChunksPerThread = 4;
+constexpr int kFlatChunksPerThread = ZERO_FLAT_CPT;
 constexpr uint64_t kFlatTileChunks = (uint64_t)kBlock * kFlatChunksPerThread;
 
 struct FlatArgs {
@@ -332,31 +350,34 @@ __global__ void __launch_bounds__(kBlock) flatten_segments(FlatArgs a)
 }
 
 // ============================================================ grad stats
-constexpr int kStatsUnroll = 4;
-constexpr int kStatsMaxBlocks = 2048;
+// One tile of kStatsTileLines 16-byte lines (8 gradients each) per block; each
+// tile leaves one fp64 partial sum of squares, and the partials are reduced in
+// a fixed order (groups of kReduceGroup, then one block), so the result is
+// bit-reproducible for a given n and 16-byte phase of the gradient buffer.
+// Overflow needs no separate flag: the square of any finite 16-bit value is
+// finite in fp64 (at most about 1.2e77), while an inf or NaN gradient makes its
+// square and hence every sum that contains it non-finite.  So the shard holds a
+// non-finite gradient exactly when the fp64 sum of squares is not finite.
+#ifndef ZERO_STATS_LINES
+#define ZERO_STATS_LINES 2   // 16-byte lines per thread in a stats tile
+#endif
+constexpr uint64_t kStatsTileLines = (uint64_t)kBlock * ZERO_STATS_LINES;
+constexpr uint64_t kReduceGroup = (uint64_t)kBlock * 16;  // partials per level-2 block
+constexpr uint64_t kFinalMax = (uint64_t)kBlock * 64;     // partials one block finishes
 
-struct Partial {
-    double sum;
-    uint32_t flag;
-    uint32_t pad;
-};
-
-// Blocks of pass 1 for n gradients: a function of n only, so the result is
-// reproducible for a given n whatever the buffer's address.
-uint32_t stats_blocks(uint64_t n)
+// Upper bound of the pass-1 tiles for n gradients at any 16-byte phase.
+uint64_t stats_tiles_max(uint64_t n)
 {
-    const uint64_t per_block = (uint64_t)kBlock * 8 * kStatsUnroll * 4;
-    uint64_t b = (n + per_block - 1) / per_block;
-    if (b < 1) b = 1;
-    if (b > kStatsMaxBlocks) b = kStatsMaxBlocks;
-    return (uint32_t)b;
+    const uint64_t lines = n / 8 + 1;
+    const uint64_t t = (lines + kStatsTileLines - 1) / kStatsTileLines;
+    return t ? t : 1;
 }
 
-template <bool BF16>
-__device__ __forceinline__ uint32_t nonfinite2(uint32_t w)  // both halves of a dword
+size_t stats_workspace_bytes(uint64_t n)
 {
-    constexpr uint32_t E = BF16 ? 0x7f80u : 0x7c00u;
-    return ((w & E) == E) | (((w >> 16) & E) == E);
+    const uint64_t t = stats_tiles_max(n);
+    const uint64_t words = t + (t + kReduceGroup - 1) / kReduceGroup;
+    return (size_t)((words * sizeof(double) + 15) / 16 * 16);
 }
 
 template <bool BF16>
@@ -368,92 +389,81 @@ __device__ __forceinline__ void accum2(uint32_t w, double &acc)
     acc = fma(b, b, acc);
 }
 
+// Sum over the block in a fixed order (butterfly within waves, then waves in
+// order); the result is valid in thread 0.
+__device__ __forceinline__ double block_sum(double x)
+{
+    __shared__ double s_part[kBlock / 64];
+    x = wave_sum(x);
+    if (threadIdx.x % 64 == 0)
+        s_part[threadIdx.x / 64] = x;
+    __syncthreads();
+    double t = 0.0;
+    if (threadIdx.x == 0)
+        for (int i = 0; i < kBlock / 64; ++i)
+            t += s_part[i];
+    return t;
+}
+
 template <bool BF16>
 __global__ void __launch_bounds__(kBlock)
     stats_pass1(const uint16_t *g, uint64_t head, uint64_t nchunks, uint64_t tail_beg, uint64_t n,
-                Partial *part)
+                double *part)
 {
     double acc = 0.0;
-    uint32_t flag = 0;
     const uint4 *lines = reinterpret_cast<const uint4 *>(g + head);
-    const uint64_t stride = (uint64_t)gridDim.x * kBlock;
-    for (uint64_t base = (uint64_t)blockIdx.x * kBlock + threadIdx.x; base < nchunks;
-         base += stride * kStatsUnroll) {
-        uint4 w[kStatsUnroll];
+    const uint64_t base = (uint64_t)blockIdx.x * kStatsTileLines + threadIdx.x;
+    uint4 w[ZERO_STATS_LINES];
 #pragma unroll
-        for (int j = 0; j < kStatsUnroll; ++j) {
-            const uint64_t c = base + j * stride;
-            w[j] = c < nchunks ? lines[c] : make_uint4(0, 0, 0, 0);
-        }
+    for (int j = 0; j < ZERO_STATS_LINES; ++j) {
+        const uint64_t c = base + (uint64_t)j * kBlock;
+        w[j] = c < nchunks ? lines[c] : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
-        for (int j = 0; j < kStatsUnroll; ++j) {
-            flag |= nonfinite2<BF16>(w[j].x) | nonfinite2<BF16>(w[j].y) |
-                    nonfinite2<BF16>(w[j].z) | nonfinite2<BF16>(w[j].w);
-            accum2<BF16>(w[j].x, acc);
-            accum2<BF16>(w[j].y, acc);
-            accum2<BF16>(w[j].z, acc);
-            accum2<BF16>(w[j].w, acc);
+    for (int j = 0; j < ZERO_STATS_LINES; ++j) {
+        accum2<BF16>(w[j].x, acc);
+        accum2<BF16>(w[j].y, acc);
+        accum2<BF16>(w[j].z, acc);
+        accum2<BF16>(w[j].w, acc);
+    }
+    if (blockIdx.x == 0) {  // elements outside the aligned lines: [0, head) and [tail_beg, n)
+        const uint64_t n_edge = head + (n - tail_beg);
+        if (threadIdx.x < n_edge) {
+            const uint64_t e = threadIdx.x < head ? threadIdx.x : tail_beg + (threadIdx.x - head);
+            const double x = (double)to_f32<BF16>(g[e]);
+            acc = fma(x, x, acc);
         }
     }
-    // elements outside the aligned lines: [0, head) and [tail_beg, n)
-    const uint64_t gid = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
-    const uint64_t n_edge = head + (n - tail_beg);
-    if (gid < n_edge) {
-        const uint32_t h = g[gid < head ? gid : tail_beg + (gid - head)];
-        flag |= nonfinite2<BF16>(h);
-        const double x = (double)to_f32<BF16>(h);
-        acc = fma(x, x, acc);
-    }
-    // block reduction in a fixed order
-    __shared__ double s_sum[kBlock / 64];
-    __shared__ uint32_t s_flag[kBlock / 64];
-    acc = wave_sum(acc);
-    flag = wave_or(flag);
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-    if (lane == 0) {
-        s_sum[wave] = acc;
-        s_flag[wave] = flag;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        double s = 0.0;
-        uint32_t f = 0;
-        for (int i = 0; i < kBlock / 64; ++i) {
-            s += s_sum[i];
-            f |= s_flag[i];
-        }
-        part[blockIdx.x] = Partial{s, f, 0};
-    }
+    const double t = block_sum(acc);
+    if (threadIdx.x == 0)
+        part[blockIdx.x] = t;
+}
+
+// Block b sums partials [b*kReduceGroup, (b+1)*kReduceGroup) in a fixed order.
+__global__ void __launch_bounds__(kBlock)
+    stats_reduce(const double *in, uint64_t n_in, double *out)
+{
+    const uint64_t lo = (uint64_t)blockIdx.x * kReduceGroup;
+    double s = 0.0;
+    for (uint64_t k = threadIdx.x; k < kReduceGroup; k += kBlock)
+        if (lo + k < n_in)
+            s += in[lo + k];
+    const double t = block_sum(s);
+    if (threadIdx.x == 0)
+        out[blockIdx.x] = t;
 }
 
 __global__ void __launch_bounds__(kBlock)
-    stats_pass2(const Partial *part, uint32_t n_part, double inv_scale_sq, zero_grad_stats_t *out)
+    stats_final(const double *in, uint64_t n_in, double inv_scale_sq, zero_grad_stats_t *out)
 {
     double s = 0.0;
-    uint32_t f = 0;
-    for (uint32_t i = threadIdx.x; i < n_part; i += kBlock) {
-        s += part[i].sum;
-        f |= part[i].flag;
-    }
-    __shared__ double s_sum[kBlock / 64];
-    __shared__ uint32_t s_flag[kBlock / 64];
-    s = wave_sum(s);
-    f = wave_or(f);
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-    if (lane == 0) {
-        s_sum[wave] = s;
-        s_flag[wave] = f;
-    }
-    __syncthreads();
+    for (uint64_t k = threadIdx.x; k < n_in; k += kBlock)
+        s += in[k];
+    const double t = block_sum(s);
     if (threadIdx.x == 0) {
-        double t = 0.0;
-        uint32_t ff = 0;
-        for (int i = 0; i < kBlock / 64; ++i) {
-            t += s_sum[i];
-            ff |= s_flag[i];
-        }
+        const bool finite = __builtin_isfinite(t);
         out->sq_norm = t * inv_scale_sq;
-        out->overflow = ff ? 1u : 0u;
+        out->overflow = finite ? 0u : 1u;
         out->pad = 0;
     }
 }
@@ -518,9 +528,15 @@ __device__ __forceinline__ void adamw_elem(const Coeffs &k, float graw, float &t
     const float g = graw * k.grad_mult;
     const float m1 = fmaf(k.b1, m, k.omb1 * g);
     const float v1 = fmaf(k.b2, v, (k.omb2 * g) * g);
+#if ZERO_FAST_SQRT_RCP
+    const float den = fmaf(__builtin_amdgcn_sqrtf(v1), k.inv_sqrt_bc2, k.eps);
+    const float ratio = m1 * __builtin_amdgcn_rcpf(den);
+#else
     const float den = fmaf(sqrtf(v1), k.inv_sqrt_bc2, k.eps);
+    const float ratio = m1 / den;
+#endif
     const float th1 = fmaf(-k.decay, th, th);
-    th = fmaf(-k.step_size, m1 / den, th1);
+    th = fmaf(-k.step_size, ratio, th1);
     m = m1;
     v = v1;
 }
@@ -545,13 +561,28 @@ __global__ void __launch_bounds__(kBlock) adamw_stream(AdamArgs a)
     const uint32_t gsb = 2 * a.g_phase;
 
     const uint64_t stride = (uint64_t)gridDim.x * kBlock;
-    for (uint64_t base = (uint64_t)blockIdx.x * kBlock + threadIdx.x; base < a.nchunks;
-         base += stride * kAdamUnroll) {
+    // chunk j of a lane's group: base + j * step
+#if ZERO_ADAM_MAPPING == 0
+    const uint64_t step = stride;
+    const uint64_t first = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
+    const uint64_t advance = stride * kAdamUnroll;
+#else
+    const uint64_t step = kBlock;
+#if ZERO_ADAM_MAPPING == 2 && ZERO_XCD_ORDER
+    const uint64_t per_xcd = (gridDim.x + 7) / 8;
+    const uint64_t tile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+#else
+    const uint64_t tile = blockIdx.x;
+#endif
+    const uint64_t first = tile * kBlock * kAdamUnroll + threadIdx.x;
+    const uint64_t advance = stride * kAdamUnroll;
+#endif
+    for (uint64_t base = first; base < a.nchunks; base += advance) {
         uint4 gw[kAdamUnroll];
         float4 th[kAdamUnroll][2], mm[kAdamUnroll][2], vv[kAdamUnroll][2];
 #pragma unroll
         for (int j = 0; j < kAdamUnroll; ++j) {
-            const uint64_t c = base + j * stride;
+            const uint64_t c = base + j * step;
             if (c < a.nchunks) {
                 if constexpr (G_ALIGNED) {
                     gw[j] = ld_stream(gl + c);
@@ -566,7 +597,7 @@ __global__ void __launch_bounds__(kBlock) adamw_stream(AdamArgs a)
         }
 #pragma unroll
         for (int j = 0; j < kAdamUnroll; ++j) {
-            const uint64_t c = base + j * stride;
+            const uint64_t c = base + j * step;
             if (c < a.nchunks) {
                 const uint32_t gws[4] = {gw[j].x, gw[j].y, gw[j].z, gw[j].w};
                 float *t = reinterpret_cast<float *>(th[j]);
@@ -659,7 +690,11 @@ inline uint32_t grid_for(uint64_t work_items, uint64_t per_block, uint32_t max_b
 template <int ES>
 zero_status flatten_launch(FlatArgs &a, hipStream_t stream)
 {
+#if ZERO_FLAT_ONESHOT
+    const uint32_t grid = grid_for(a.tile_lo[a.n_segs], 1, 0x7ffffff0u);
+#else
     const uint32_t grid = grid_for(a.tile_lo[a.n_segs], 1, resident_blocks(flatten_segments<ES>));
+#endif
     hipLaunchKernelGGL(flatten_segments<ES>, dim3(grid), dim3(kBlock), 0, stream, a);
     return launch_status("zero_bucket_flatten");
 }
@@ -754,7 +789,7 @@ extern "C" zero_status zero_grad_stats_workspace(uint64_t n, size_t *bytes)
 {
     if (!bytes)
         return fail(ZERO_EINVAL, "zero_grad_stats_workspace: NULL output");
-    *bytes = (size_t)stats_blocks(n) * sizeof(Partial);
+    *bytes = stats_workspace_bytes(n);
     return ZERO_OK;
 }
 
@@ -770,12 +805,13 @@ extern "C" zero_status zero_grad_stats(const void *grad, zero_dtype gdt, uint64_
         return fail(ZERO_EINVAL, "zero_grad_stats: inv_loss_scale must be finite and > 0");
     if (n > 0 && !grad)
         return fail(ZERO_EINVAL, "zero_grad_stats: NULL grad");
+    if (n > UINT64_MAX / 4)
+        return fail(ZERO_EINVAL, "zero_grad_stats: n too large");
     if (!workspace)
         return fail(ZERO_EINVAL, "zero_grad_stats: NULL workspace");
-    const uint32_t blocks = stats_blocks(n);
-    if (ws_bytes < (size_t)blocks * sizeof(Partial))
-        return fail(ZERO_ENOSPC, "zero_grad_stats: workspace %zu bytes < %zu", ws_bytes,
-                    (size_t)blocks * sizeof(Partial));
+    const size_t need = stats_workspace_bytes(n);
+    if (ws_bytes < need)
+        return fail(ZERO_ENOSPC, "zero_grad_stats: workspace %zu bytes < %zu", ws_bytes, need);
     if (!aligned(grad, 2) || !aligned(workspace, 16) || !aligned(d_stats, 8))
         return fail(ZERO_EALIGN, "zero_grad_stats: misaligned pointer");
     if (overlap(workspace, ws_bytes, d_stats, sizeof *d_stats) ||
@@ -787,20 +823,37 @@ extern "C" zero_status zero_grad_stats(const void *grad, zero_dtype gdt, uint64_
     if (head > n) head = n;
     const uint64_t nchunks = (n - head) / 8;
     const uint64_t tail_beg = head + 8 * nchunks;
-    Partial *part = (Partial *)workspace;
+    uint64_t tiles = (nchunks + kStatsTileLines - 1) / kStatsTileLines;
+    if (tiles == 0) tiles = 1;  // block 0 also takes the elements outside the lines
+    if (tiles > 0x7fffffffu)
+        return fail(ZERO_EINVAL, "zero_grad_stats: n too large for one call");
+    double *part = (double *)workspace;
     const uint16_t *g = (const uint16_t *)grad;
     if (gdt == ZERO_BF16)
-        hipLaunchKernelGGL(stats_pass1<true>, dim3(blocks), dim3(kBlock), 0, s, g, head, nchunks,
-                           tail_beg, n, part);
+        hipLaunchKernelGGL(stats_pass1<true>, dim3((uint32_t)tiles), dim3(kBlock), 0, s, g, head,
+                           nchunks, tail_beg, n, part);
     else
-        hipLaunchKernelGGL(stats_pass1<false>, dim3(blocks), dim3(kBlock), 0, s, g, head, nchunks,
-                           tail_beg, n, part);
+        hipLaunchKernelGGL(stats_pass1<false>, dim3((uint32_t)tiles), dim3(kBlock), 0, s, g, head,
+                           nchunks, tail_beg, n, part);
     zero_status st = launch_status("zero_grad_stats pass 1");
     if (st != ZERO_OK)
         return st;
-    hipLaunchKernelGGL(stats_pass2, dim3(1), dim3(kBlock), 0, s, (const Partial *)part, blocks,
+    const double *last = part;
+    uint64_t n_last = tiles;
+    if (tiles > kFinalMax) {
+        double *part2 = part + tiles;
+        const uint64_t groups = (tiles + kReduceGroup - 1) / kReduceGroup;
+        hipLaunchKernelGGL(stats_reduce, dim3((uint32_t)groups), dim3(kBlock), 0, s,
+                           (const double *)part, tiles, part2);
+        st = launch_status("zero_grad_stats reduce");
+        if (st != ZERO_OK)
+            return st;
+        last = part2;
+        n_last = groups;
+    }
+    hipLaunchKernelGGL(stats_final, dim3(1), dim3(kBlock), 0, s, last, n_last,
                        inv_loss_scale * inv_loss_scale, d_stats);
-    return launch_status("zero_grad_stats pass 2");
+    return launch_status("zero_grad_stats final");
 }
 
 namespace {
@@ -808,7 +861,18 @@ template <bool GB, bool PB, bool GA, bool PA>
 void launch_adam_variant(const AdamArgs &a, uint64_t work, hipStream_t s)
 {
     auto kernel = adamw_stream<GB, PB, GA, PA>;
-    const uint32_t grid = grid_for(work, (uint64_t)kBlock * kAdamUnroll, resident_blocks(kernel));
+    const uint64_t per_block = (uint64_t)kBlock * kAdamUnroll;
+#if ZERO_ADAM_MAPPING == 2
+    // one tile per block; the element-wise fallback keeps a resident grid
+    uint32_t grid = a.nchunks ? grid_for(a.nchunks, per_block, 0x7ffffff0u)
+                              : grid_for(work, per_block, resident_blocks(kernel));
+#if ZERO_XCD_ORDER
+    if (a.nchunks)
+        grid = (grid + 7) / 8 * 8;  // whole rounds of the 8 XCDs; spare blocks find no tile
+#endif
+#else
+    const uint32_t grid = grid_for(work, per_block, resident_blocks(kernel));
+#endif
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), 0, s, a);
 }
 
