@@ -2,16 +2,19 @@
 
 A step is one pass of the whole hot path over one batch of synthetic
 gradients already resident in HBM:
-  host plan (zero_partition, zero_bucket_plan)
-  -> zero_bucket_flatten: per-tensor 16-bit grads into the flat grad shard,
-     one call per constant-size fused buffer (500M elements)
-  -> zero_grad_stats: overflow flag + squared norm (fp64)
+  zero_partition (host)
+  -> zero_bucket_flatten_stats: the rank's per-tensor 16-bit grads gathered
+     into the flat grad shard, with the overflow flag and squared norm (fp64)
+     computed in the same pass (at Nd = 1 the per-tensor grads are final)
   -> zero_adam_step: fused AdamW on fp32 master/m/v, writes 16-bit params
+With --unfused the gather runs once per 500M-element fused buffer
+(zero_bucket_flatten) followed by a separate zero_grad_stats pass.
 Workload: GPT-2-1.5B-like parameter list (48 layers, hidden 1600, vocab
 50257, fp16) at Nd=1, so the rank's shard is all 1,557,611,200 parameters;
 loss scale 2^16, clip 1.0.
 
-Prints one JSON line.  `value` is parameters per second of the whole step;
+Prints one JSON line.  `value` is parameters per second of the whole step
+(32 B/param fused, 34 unfused);
 the roofline object covers the fused AdamW kernel (28 algorithmic bytes per
 parameter: read grad 2 + master/m/v 12, write master/m/v 12 + param 2).
 """
@@ -76,30 +79,41 @@ class Workload:
         self.stats = z.new_grad_stats(device)
         self.state = z.new_adam_state(device)
         self.ws = z.new_workspace(n, device)
+        nb = z.zero_bucket_flatten_stats_workspace(cfg.numels, self.begin, n)
+        self.fws = torch.empty(nb, dtype=torch.uint8, device=device)
         self.hp = z.adamw(**cfg.hp.__dict__)
         self.ptrs = [t.data_ptr() if t is not None else None for t in self.grads]
         torch.cuda.synchronize()
         log(f"[bench] inputs resident in HBM after {time.time() - t0:.1f}s "
             f"({torch.cuda.memory_allocated() / 1e9:.1f} GB allocated)")
 
-    def step(self, ev=None):
+    def step(self, ev=None, fused=True):
         """One pass of the hot path; ev: optional list of 4 events recorded
-        around flatten / stats / adam on the launch stream."""
+        around gather / stats / adam on the launch stream.  fused: gather the
+        rank's gradients and compute their statistics in one pass (the rank's
+        per-tensor gradients are final at Nd = 1); otherwise gather one fused
+        buffer at a time, then a separate statistics pass."""
         z, cfg = self.z, self.cfg
         stream = self.torch.cuda.current_stream()
         s = stream.cuda_stream
         b, e = z.zero_partition(cfg.psi, cfg.nd, cfg.rank)
         B = cfg.bucket_elems or cfg.psi
         if ev: ev[0].record(stream)
-        lo = b
-        while lo < e:  # one fused buffer at a time, this rank's part of it
-            hi = min((lo // B + 1) * B, e)
-            z.zero_bucket_flatten(self.ptrs, cfg.numels, cfg.dtype, lo, hi - lo,
-                                  self.g.data_ptr() + 2 * (lo - b), s)
-            lo = hi
-        if ev: ev[1].record(stream)
-        z.zero_grad_stats(self.g, cfg.dtype, self.n, cfg.hp.inv_loss_scale, self.ws,
-                          self.ws.numel(), self.stats, s)
+        if fused:
+            z.zero_bucket_flatten_stats(self.ptrs, cfg.numels, cfg.dtype, b, e - b, self.g,
+                                        cfg.hp.inv_loss_scale, self.fws, self.fws.numel(),
+                                        self.stats, s)
+            if ev: ev[1].record(stream)
+        else:
+            lo = b
+            while lo < e:  # one fused buffer at a time, this rank's part of it
+                hi = min((lo // B + 1) * B, e)
+                z.zero_bucket_flatten(self.ptrs, cfg.numels, cfg.dtype, lo, hi - lo,
+                                      self.g.data_ptr() + 2 * (lo - b), s)
+                lo = hi
+            if ev: ev[1].record(stream)
+            z.zero_grad_stats(self.g, cfg.dtype, self.n, cfg.hp.inv_loss_scale, self.ws,
+                              self.ws.numel(), self.stats, s)
         if ev: ev[2].record(stream)
         z.zero_adam_step(self.hp, self.g, cfg.dtype, self.master, self.m, self.v, self.p,
                          cfg.dtype, self.n, self.stats, self.state, s)
@@ -188,6 +202,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time plain device copies of a known size instead")
+    ap.add_argument("--unfused", action="store_true",
+                    help="gather per fused buffer, then a separate statistics pass")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one data-parallel rank's shard on one GPU; runs on more "
@@ -203,8 +219,9 @@ def main():
     torch.cuda.set_device(dev)
     w = Workload(args.config, dev)
 
+    fused = not args.unfused
     for _ in range(args.warmup):
-        w.step()
+        w.step(fused=fused)
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done")
 
@@ -212,13 +229,13 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        w.step(evs[k])
+        w.step(evs[k], fused=fused)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = np.array([[a.elapsed_time(b) for a, b in zip(e[:-1], e[1:])] for e in evs])
     flat_ms, stats_ms, adam_ms = ms.mean(axis=0)
-    log(f"[bench] timed {args.steps} steps in {wall:.3f}s; per step flatten {flat_ms:.3f} ms, "
-        f"stats {stats_ms:.3f} ms, adam {adam_ms:.3f} ms "
+    log(f"[bench] timed {args.steps} steps in {wall:.3f}s ({'fused' if fused else 'unfused'}); "
+        f"per step gather {flat_ms:.3f} ms, stats {stats_ms:.3f} ms, adam {adam_ms:.3f} ms "
         f"(adam min {ms[:, 2].min():.3f} max {ms[:, 2].max():.3f})")
     # every step must have been a real update: the device step counter counts them
     st = w.z.read_adam_state(w.state)
@@ -231,6 +248,23 @@ def main():
 
     n = w.n
     step_ms = wall * 1e3 / args.steps
+    kernels = {"adam_step": {"ms": adam_ms, "ms_min": float(ms[:, 2].min()),
+                             "ms_max": float(ms[:, 2].max()), "params_per_s": n / (adam_ms * 1e-3),
+                             "GB/s": ADAM_BYTES_PER_PARAM * n / (adam_ms * 1e-3) / 1e9,
+                             "bytes_per_param": ADAM_BYTES_PER_PARAM}}
+    if fused:  # gather + statistics in one pass: 2 B read + 2 B written per param
+        kernels["bucket_flatten_stats"] = {
+            "ms": flat_ms, "GB/s": FLATTEN_BYTES_PER_PARAM * n / (flat_ms * 1e-3) / 1e9,
+            "bytes_per_param": FLATTEN_BYTES_PER_PARAM}
+        step_bytes = ADAM_BYTES_PER_PARAM + FLATTEN_BYTES_PER_PARAM
+    else:
+        kernels["bucket_flatten"] = {
+            "ms": flat_ms, "GB/s": FLATTEN_BYTES_PER_PARAM * n / (flat_ms * 1e-3) / 1e9,
+            "bytes_per_param": FLATTEN_BYTES_PER_PARAM}
+        kernels["grad_stats"] = {
+            "ms": stats_ms, "GB/s": STATS_BYTES_PER_PARAM * n / (stats_ms * 1e-3) / 1e9,
+            "bytes_per_param": STATS_BYTES_PER_PARAM}
+        step_bytes = ADAM_BYTES_PER_PARAM + STATS_BYTES_PER_PARAM + FLATTEN_BYTES_PER_PARAM
     adam_gbs = ADAM_BYTES_PER_PARAM * n / (adam_ms * 1e-3) / 1e9
     traffic = load_traffic(n)
     out = {
@@ -253,19 +287,8 @@ def main():
                    "loss_scale": w.cfg.loss_scale},
         "roofline": {"bound": "hbm", "achieved": adam_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": adam_gbs / HBM_PEAK_GBS, "traffic": traffic},
-        "kernels": {
-            "adam_step": {"ms": adam_ms, "ms_min": float(ms[:, 2].min()),
-                          "ms_max": float(ms[:, 2].max()), "params_per_s": n / (adam_ms * 1e-3),
-                          "GB/s": adam_gbs, "bytes_per_param": ADAM_BYTES_PER_PARAM},
-            "grad_stats": {"ms": stats_ms,
-                           "GB/s": STATS_BYTES_PER_PARAM * n / (stats_ms * 1e-3) / 1e9,
-                           "bytes_per_param": STATS_BYTES_PER_PARAM},
-            "bucket_flatten": {"ms": flat_ms,
-                               "GB/s": FLATTEN_BYTES_PER_PARAM * n / (flat_ms * 1e-3) / 1e9,
-                               "bytes_per_param": FLATTEN_BYTES_PER_PARAM},
-        },
-        "step_bytes_per_param": ADAM_BYTES_PER_PARAM + STATS_BYTES_PER_PARAM +
-                                FLATTEN_BYTES_PER_PARAM,
+        "kernels": kernels,
+        "step_bytes_per_param": step_bytes,
         "checks": {"device_steps_taken": int(st.step), "overflow": int(gs.overflow),
                    "sq_norm": gs.sq_norm, "clip_coef": st.coef},
     }

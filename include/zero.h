@@ -158,6 +158,31 @@ zero_status zero_grad_stats(const void *grad, zero_dtype gdt, uint64_t n, double
                             void *workspace, size_t ws_bytes, zero_grad_stats_t *d_stats,
                             void *stream);
 
+/* Bytes of device workspace that zero_bucket_flatten_stats needs for the
+ * elements [range_begin, range_begin + count) of the tensors numel[]. */
+zero_status zero_bucket_flatten_stats_workspace(const uint64_t *numel, uint32_t n_tensors,
+                                                uint64_t range_begin, uint64_t count,
+                                                size_t *bytes);
+
+/* zero_bucket_flatten fused with zero_grad_stats: gathers the elements
+ * [range_begin, range_begin + count) of the list-order flat stream of 16-bit
+ * gradient tensors into dst ([P2] ZeRO-R, CB) and, in the same pass, writes
+ * *d_stats for the gathered values exactly as zero_grad_stats would for dst
+ * (overflow flag; squared L2 norm of g * inv_loss_scale in fp64, summed in a
+ * fixed order that depends only on the tensor sizes, the range and dst's
+ * 16-byte phase).  Each gradient is read from HBM once instead of twice.  For
+ * callers whose gathered range is the rank's final gradient shard: a single
+ * data-parallel rank, or gradients already reduced into the per-tensor
+ * buffers.  gdt: F16 or BF16.  workspace: device memory of at least
+ * zero_bucket_flatten_stats_workspace(...) bytes, 16-byte aligned.
+ * count == 0 writes {0, 0}.  Errors: as zero_bucket_flatten and
+ * zero_grad_stats (ZERO_EINVAL, ZERO_ENOSPC, ZERO_EALIGN, ZERO_EDEVICE). */
+zero_status zero_bucket_flatten_stats(const void *const *tensor_ptrs, const uint64_t *numel,
+                                      uint32_t n_tensors, zero_dtype gdt, uint64_t range_begin,
+                                      uint64_t count, void *dst, double inv_loss_scale,
+                                      void *workspace, size_t ws_bytes, zero_grad_stats_t *d_stats,
+                                      void *stream);
+
 /* AdamW hyper-parameters (host memory, fp64). */
 typedef struct {
     double lr, beta1, beta2, eps, weight_decay;

@@ -23,7 +23,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     assert set(names) == set(z.EXPORTS)
     L = ctypes.CDLL(z.LIB_PATH)
     for name in names:
@@ -212,3 +212,31 @@ def test_flatten_validation():
     assert _status(z.zero_bucket_flatten, ts, numel, "f16", 290, 20, dst, 0) == z.ZERO_EINVAL
     # dst inside a source tensor
     assert _status(z.zero_bucket_flatten, ts, numel, "f16", 0, 10, FAKE + 8, 0) == z.ZERO_EINVAL
+
+
+def test_flatten_stats_validation():
+    ts = [FAKE, FAKE + (1 << 20), None]
+    numel = [100, 200, 50]
+    dst, ws, st_ = FAKE + (8 << 20), FAKE + (12 << 20), FAKE + (16 << 20)
+    need = z.zero_bucket_flatten_stats_workspace(numel, 0, 300)
+    assert need >= 16 and need % 16 == 0
+    call = z.zero_bucket_flatten_stats
+    assert _status(call, ts, numel, "f16", 0, 300, dst, 1.0, ws, need - 16, st_, 0) == z.ZERO_ENOSPC
+    assert _status(call, ts, numel, "f32", 0, 300, dst, 1.0, ws, need, st_, 0) == z.ZERO_EINVAL
+    assert _status(call, ts, numel, "f16", 0, 300, dst, 0.0, ws, need, st_, 0) == z.ZERO_EINVAL
+    assert _status(call, ts, numel, "f16", 0, 300, dst, 1.0, ws, need, None, 0) == z.ZERO_EINVAL
+    assert _status(call, ts, numel, "f16", 0, 300, dst, 1.0, None, need, st_, 0) == z.ZERO_EINVAL
+    assert _status(call, ts, numel, "f16", 0, 300, dst, 1.0, ws + 8, need, st_, 0) == z.ZERO_EALIGN
+    assert _status(call, ts, numel, "f16", 0, 300, dst, 1.0, dst + 64, need, st_, 0) == z.ZERO_EINVAL
+    assert _status(call, ts, numel, "bf16", 250, 60, dst, 1.0, ws, need, st_, 0) == z.ZERO_EINVAL
+    assert _status(call, ts, numel, "bf16", 290, 20, dst, 1.0, ws, need, st_, 0) == z.ZERO_EINVAL
+
+
+def test_flatten_stats_workspace_bound():
+    """The workspace covers every tile at any destination phase: one partial
+    per 256 full lines of each tensor piece (at least one per piece), plus
+    the second reduction level."""
+    numel = [1, 7, 8, 9, 4096, 2049 * 8, 3]
+    got = z.zero_bucket_flatten_stats_workspace(numel, 0, sum(numel))
+    tiles = sum(max(1, -(-(k // 8) // 256)) for k in numel)
+    assert got >= 8 * tiles

@@ -98,10 +98,21 @@ class Rank:
                                   self.g.data_ptr() + 2 * (lo - self.begin))
             lo = hi
 
-    def stats_and_step(self):
+    def gather_with_stats(self, grads):
+        """The whole shard gathered in one pass that also writes the
+        statistics (the path of a rank whose per-tensor gradients are final)."""
         cfg = self.cfg
-        z.zero_grad_stats(self.g, cfg.dtype, self.n, cfg.hp.inv_loss_scale, self.ws,
-                          self.ws.numel(), self.stats)
+        ptrs = [grads[i].data_ptr() if i in grads else None for i in range(len(cfg.numels))]
+        nb = z.zero_bucket_flatten_stats_workspace(cfg.numels, self.begin, self.n)
+        self.fws = torch.empty(nb, dtype=torch.uint8, device=dev())
+        z.zero_bucket_flatten_stats(ptrs, cfg.numels, cfg.dtype, self.begin, self.n, self.g,
+                                    cfg.hp.inv_loss_scale, self.fws, nb, self.stats)
+
+    def stats_and_step(self, fused=False):
+        cfg = self.cfg
+        if not fused:
+            z.zero_grad_stats(self.g, cfg.dtype, self.n, cfg.hp.inv_loss_scale, self.ws,
+                              self.ws.numel(), self.stats)
         z.zero_adam_step(self.hp, self.g, cfg.dtype, self.master, self.m, self.v, self.p,
                          cfg.dtype, self.n, self.stats, self.state)
 
@@ -119,7 +130,8 @@ def _oracle_norm_streamed(g_dev, dtype, inv, chunk=1 << 29):
 
 
 # ------------------------------------------------------------ workload 1
-def test_workload1_tiny_full():
+@pytest.mark.parametrize("fused", [False, True])
+def test_workload1_tiny_full(fused):
     cfg = CONFIGS[1]
     r = Rank(cfg)
     n, b, e = r.n, r.begin, r.end
@@ -136,11 +148,14 @@ def test_workload1_tiny_full():
     for k in range(cfg.steps):
         host = gen.host_grad_list(cfg, k)
         grads = {i: torch.from_numpy(h.view(np.int16)).to(dev()) for i, h in enumerate(host)}
-        r.gather(grads)
+        if fused:
+            r.gather_with_stats(grads)
+        else:
+            r.gather(grads)
         g_ref = oracle.flatten(host, b, e)
         assert np.array_equal(_to_host16(r.g), g_ref), k
         th0, m0, v0 = (a.cpu().numpy().copy() for a in (r.master, r.m, r.v))
-        r.stats_and_step()
+        r.stats_and_step(fused)
         torch.cuda.synchronize()
         st = z.read_grad_stats(r.stats)
         sq, ov = oracle.grad_stats(g_ref, cfg.dtype, cfg.hp.inv_loss_scale)
@@ -172,7 +187,8 @@ def _w5_grads(cfg, r, step):
 
 
 @pytest.mark.timeout(900)
-def test_workload5_shard_skip_full():
+@pytest.mark.parametrize("fused", [False, True])
+def test_workload5_shard_skip_full(fused):
     cfg = CONFIGS[5]
     r = Rank(cfg, p_phase=oracle.partition(cfg.psi, cfg.nd, cfg.rank)[0] % 8)
     n, b = r.n, r.begin
@@ -186,7 +202,17 @@ def test_workload5_shard_skip_full():
     t_expect = 0
     for k in range(cfg.steps):
         grads = _w5_grads(cfg, r, k)
-        r.gather(grads)
+        if k == inj_step:  # the non-finite values are planted in the per-tensor inputs
+            offs = np.cumsum([0] + cfg.numels)
+            for i, bits in inj:
+                gi = b + i  # flat position -> tensor and offset
+                ti = int(np.searchsorted(offs, gi, side="right") - 1)
+                o = gi - int(offs[ti])
+                grads[ti][o:o + 1] = _dev16(bits, grads[ti])
+        if fused:
+            r.gather_with_stats(grads)
+        else:
+            r.gather(grads)
         # the gathered shard against the oracle's flatten of the same tensors
         host = {i: _to_host16(t) for i, t in grads.items()}
         lo_t = int(np.cumsum([0] + cfg.numels)[r.tensor_ids[0]])
@@ -194,13 +220,11 @@ def test_workload5_shard_skip_full():
         g_ref = oracle.flatten(sub, b - lo_t, r.end - lo_t)
         del host, sub
         if k == inj_step:
-            for i, bits in inj:
-                r.g[i:i + 1] = _dev16(bits, r.g)
-                g_ref[i] = bits
+            assert all(g_ref[i] == bits for i, bits in inj)
         assert np.array_equal(_to_host16(r.g), g_ref), k
         th0, m0, v0 = (a.cpu().numpy().copy() for a in (r.master, r.m, r.v))
         p_before = _to_host16(r.p).copy()
-        r.stats_and_step()
+        r.stats_and_step(fused)
         torch.cuda.synchronize()
         st = z.read_grad_stats(r.stats)
         sq, ov = oracle.grad_stats(g_ref, cfg.dtype, cfg.hp.inv_loss_scale)

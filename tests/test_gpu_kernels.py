@@ -335,3 +335,70 @@ def test_param_rounding_every_tie(dtype):
     bad = np.nonzero(got != ref)[0]
     assert bad.size == 0, [(float(x[i]), hex(got[i]), hex(ref[i])) for i in bad[:5]]
     assert p.canaries_intact()
+
+
+# ------------------------------------------------- gather fused with stats
+def _fused(srcs, numels, dtype, lo, hi, dst, inv):
+    ws_bytes = z.zero_bucket_flatten_stats_workspace(numels, lo, hi - lo)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev())
+    stats = z.new_grad_stats(dev())
+    z.zero_bucket_flatten_stats([s.ptr() if s is not None else None for s in srcs], numels, dtype,
+                                lo, hi - lo, dst.ptr(), inv, ws, ws_bytes, stats)
+    return z.read_grad_stats(stats)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("dst_phase", [0, 3, 7])
+def test_flatten_stats_parity(dtype, dst_phase):
+    rng = np.random.default_rng(200 + dst_phase)
+    numels = [1, 7, 8, 9, 3, 1000, 4099, 70_001, 2, 16, 33, 262_145, 5, 600_000]
+    host = [gen.f32_to_bits16((rng.standard_normal(k) * 5).astype(np.float32), dtype)
+            for k in numels]
+    srcs = [Guarded(k, np.uint16, phase=(i * 5) % 8, init=h) for i, (k, h) in
+            enumerate(zip(numels, host))]
+    psi = sum(numels)
+    inv = 2.0 ** -3
+    for lo, hi in [(0, psi), (3, psi - 2), (17, 17 + 5000), (psi - 1, psi), (1009, 1009 + 262_145)]:
+        dst = Guarded(hi - lo, np.uint16, phase=dst_phase)
+        st = _fused(srcs, numels, dtype, lo, hi, dst, inv)
+        torch.cuda.synchronize()
+        ref = oracle.flatten(host, lo, hi)
+        assert np.array_equal(dst.host(), ref), (lo, hi)
+        sq, ov = oracle.grad_stats(ref, dtype, inv)
+        assert st.overflow == ov == 0 and abs(st.sq_norm - sq) <= 1e-12 * sq, (lo, hi)
+        # the same value zero_grad_stats reports for the gathered buffer
+        st2 = _stats(dst, dtype, hi - lo, inv)
+        assert abs(st2.sq_norm - st.sq_norm) <= 1e-14 * sq and st2.overflow == 0
+        assert dst.canaries_intact()
+        st3 = _fused(srcs, numels, dtype, lo, hi, dst, inv)  # bit-reproducible
+        assert st3.sq_norm == st.sq_norm
+    assert all(s.canaries_intact() for s in srcs)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_flatten_stats_overflow_and_many_segments(dtype):
+    rng = np.random.default_rng(9)
+    numels = [int(k) for k in rng.integers(1, 3000, 300)]   # several launches of segments
+    host = [gen.f32_to_bits16(rng.standard_normal(k).astype(np.float32), dtype) for k in numels]
+    psi = sum(numels)
+    pinf, ninf, nan = gen.specials(dtype)
+    srcs = [Guarded(k, np.uint16, phase=i % 8, init=h) for i, (k, h) in enumerate(zip(numels, host))]
+    dst = Guarded(psi, np.uint16, phase=1)
+    st = _fused(srcs, numels, dtype, 0, psi, dst, 1.0)
+    sq, ov = oracle.grad_stats(oracle.flatten(host, 0, psi), dtype, 1.0)
+    assert st.overflow == ov == 0 and abs(st.sq_norm - sq) <= 1e-12 * sq
+    offs = np.cumsum([0] + numels)
+    for ti, pos, special in [(0, 0, pinf), (150, numels[150] // 2, nan), (299, numels[299] - 1, ninf),
+                             (77, 0, nan | 0x8000)]:
+        h = host[ti].copy()
+        h[pos] = special
+        src = Guarded(numels[ti], np.uint16, phase=ti % 8, init=h)
+        ss = list(srcs)
+        ss[ti] = src
+        st = _fused(ss, numels, dtype, 0, psi, dst, 1.0)
+        assert st.overflow == 1, (ti, pos)
+        g = dst.host()
+        assert g[offs[ti] + pos] == special
+    # empty range writes {0, 0}
+    st = _fused(srcs, numels, dtype, 10, 10, dst, 1.0)
+    assert st.overflow == 0 and st.sq_norm == 0.0

@@ -59,7 +59,8 @@ assert ctypes.sizeof(GradStats) == 16 and ctypes.sizeof(AdamState) == 64
 
 EXPORTS = ("zero_status_str", "zero_last_error", "zero_partition", "zero_mem_bytes",
            "zero_bucket_plan", "zero_bucket_flatten", "zero_grad_stats_workspace",
-           "zero_grad_stats", "zero_adam_step")
+           "zero_grad_stats", "zero_bucket_flatten_stats_workspace", "zero_bucket_flatten_stats",
+           "zero_adam_step")
 
 _lib = None
 
@@ -84,6 +85,11 @@ def lib():
                                           ctypes.c_int, U64, U64, VP, VP]
         L.zero_grad_stats_workspace.argtypes = [U64, ctypes.POINTER(ctypes.c_size_t)]
         L.zero_grad_stats.argtypes = [VP, ctypes.c_int, U64, DBL, VP, ctypes.c_size_t, VP, VP]
+        L.zero_bucket_flatten_stats_workspace.argtypes = [ctypes.POINTER(U64), U32, U64, U64,
+                                                          ctypes.POINTER(ctypes.c_size_t)]
+        L.zero_bucket_flatten_stats.argtypes = [ctypes.POINTER(VP), ctypes.POINTER(U64), U32,
+                                                ctypes.c_int, U64, U64, VP, DBL, VP,
+                                                ctypes.c_size_t, VP, VP]
         L.zero_adam_step.argtypes = [ctypes.POINTER(AdamW), VP, ctypes.c_int, VP, VP, VP, VP,
                                      ctypes.c_int, U64, VP, VP, VP]
         for name in EXPORTS[2:]:
@@ -174,6 +180,27 @@ def zero_grad_stats(grad, gdtype, n: int, inv_loss_scale: float, workspace, ws_b
                     d_stats, stream=None) -> None:
     _check(lib().zero_grad_stats(_ptr(grad), _dtype(gdtype), n, inv_loss_scale, _ptr(workspace),
                                  ws_bytes, _ptr(d_stats), _stream(stream)))
+
+
+def zero_bucket_flatten_stats_workspace(numel: Sequence[int], range_begin: int,
+                                        count: int) -> int:
+    nums = (U64 * len(numel))(*numel)
+    out = ctypes.c_size_t()
+    _check(lib().zero_bucket_flatten_stats_workspace(nums, len(numel), range_begin, count,
+                                                     ctypes.byref(out)))
+    return out.value
+
+
+def zero_bucket_flatten_stats(tensors: Sequence, numel: Optional[Sequence[int]], gdtype,
+                              range_begin: int, count: int, dst, inv_loss_scale: float,
+                              workspace, ws_bytes: int, d_stats, stream=None) -> None:
+    if numel is None:
+        numel = [t.numel() for t in tensors]
+    ptrs = (VP * len(tensors))(*[_ptr(t) for t in tensors])
+    nums = (U64 * len(numel))(*numel)
+    _check(lib().zero_bucket_flatten_stats(ptrs, nums, len(tensors), _dtype(gdtype), range_begin,
+                                           count, _ptr(dst), inv_loss_scale, _ptr(workspace),
+                                           ws_bytes, _ptr(d_stats), _stream(stream)))
 
 
 def zero_adam_step(hp: AdamW, grad, gdtype, master, exp_avg, exp_avg_sq, param_out, pdtype,

@@ -245,8 +245,14 @@ constexpr int kMaxSegs = 96;         // segments per launch (kernel-argument tab
 constexpr int kFlatChunksPerThread = ZERO_FLAT_CPT;
 constexpr uint64_t kFlatTileChunks = (uint64_t)kBlock * kFlatChunksPerThread;
 
+// Gather modes: a plain copy, or a copy that also sums the squares of the
+// 16-bit values each tile writes (fp16 or bf16), one fp64 partial per tile.
+enum { kCopy = 0, kStatsF16 = 1, kStatsBF16 = 2 };
+
 struct FlatArgs {
     char *dst;                     // element 0 of the destination range
+    double *part;                  // per-tile partial sums (stats modes)
+    uint64_t tile_base;            // global index of this launch's first tile
     uint32_t n_segs;
     uint32_t dst_phase;            // (dst address mod 16) / element size
     uint64_t seg_lo[kMaxSegs + 1]; // destination element offset of each segment
@@ -254,9 +260,35 @@ struct FlatArgs {
     const char *src[kMaxSegs];     // address of each segment's first source element
 };
 
-template <int ES, int SB>
+template <bool BF16>
+__device__ __forceinline__ void accum2(uint32_t w, double &acc)
+{
+    const double a = (double)to_f32<BF16>(w & 0xffffu);
+    const double b = (double)hi_to_f32<BF16>(w);
+    acc = fma(a, a, acc);  // squares of 16-bit values are exact in fp64
+    acc = fma(b, b, acc);
+}
+
+// Sum over the block in a fixed order (butterfly within waves, then waves in
+// order); the result is valid in thread 0.  Safe to call once per loop trip.
+__device__ __forceinline__ double block_sum(double x)
+{
+    __shared__ double s_part[kBlock / 64];
+    x = wave_sum(x);
+    if (threadIdx.x % 64 == 0)
+        s_part[threadIdx.x / 64] = x;
+    __syncthreads();
+    double t = 0.0;
+    if (threadIdx.x == 0)
+        for (int i = 0; i < kBlock / 64; ++i)
+            t += s_part[i];
+    __syncthreads();  // s_part is free again for the next call
+    return t;
+}
+
+template <int ES, int SB, int MODE>
 __device__ __forceinline__ void flatten_full_chunks(const char *src_line0, char *dst_line0,
-                                                    uint64_t c_beg, uint64_t c_end)
+                                                    uint64_t c_beg, uint64_t c_end, double &acc)
 {
     // chunk c (relative to the segment's first full chunk) reads the aligned
     // source lines c and c+1 (shifted by SB bytes) and writes destination line c
@@ -281,11 +313,17 @@ __device__ __forceinline__ void flatten_full_chunks(const char *src_line0, char 
             else
                 o = shift_lines<SB>(lo[j], hi[j]);
             reinterpret_cast<uint4 *>(dst_line0)[c] = o;
+            if constexpr (MODE != kCopy) {
+                accum2<MODE == kStatsBF16>(o.x, acc);
+                accum2<MODE == kStatsBF16>(o.y, acc);
+                accum2<MODE == kStatsBF16>(o.z, acc);
+                accum2<MODE == kStatsBF16>(o.w, acc);
+            }
         }
     }
 }
 
-template <int ES>
+template <int ES, int MODE>
 __global__ void __launch_bounds__(kBlock) flatten_segments(FlatArgs a)
 {
     constexpr uint64_t V = 16 / ES;  // elements per 16-byte line
@@ -305,6 +343,7 @@ __global__ void __launch_bounds__(kBlock) flatten_segments(FlatArgs a)
         const bool has_full = c1 > c0;
         const uint64_t k = tile - a.tile_lo[s];
         const char *src = a.src[s];
+        double acc = 0.0;
         if (k == 0) {
             // partial lines at both ends, element by element
             const uint64_t head_end = has_full ? c0 * V - ph : e_hi;
@@ -313,38 +352,49 @@ __global__ void __launch_bounds__(kBlock) flatten_segments(FlatArgs a)
             const uint64_t i = threadIdx.x;
             if (i < n_head + n_tail) {
                 const uint64_t e = i < n_head ? e_lo + i : tail_beg + (i - n_head);
-                if constexpr (ES == 2)
-                    reinterpret_cast<uint16_t *>(a.dst)[e] =
-                        reinterpret_cast<const uint16_t *>(src)[e - e_lo];
-                else
+                if constexpr (ES == 2) {
+                    const uint16_t v = reinterpret_cast<const uint16_t *>(src)[e - e_lo];
+                    reinterpret_cast<uint16_t *>(a.dst)[e] = v;
+                    if constexpr (MODE != kCopy) {
+                        const double x = (double)to_f32<MODE == kStatsBF16>(v);
+                        acc = fma(x, x, acc);
+                    }
+                } else {
                     reinterpret_cast<uint32_t *>(a.dst)[e] =
                         reinterpret_cast<const uint32_t *>(src)[e - e_lo];
-            }
-        }
-        if (!has_full)
-            continue;
-        const uint64_t t_beg = k * kFlatTileChunks;
-        const uint64_t t_end = (t_beg + kFlatTileChunks < c1 - c0) ? t_beg + kFlatTileChunks : c1 - c0;
-        // first full line's source bytes and their 16-byte phase (uniform)
-        const uintptr_t s0 = (uintptr_t)(src + (c0 * V - ph - e_lo) * ES);
-        const uint32_t sb = (uint32_t)(s0 & 15u);
-        const char *src_line0 = (const char *)(s0 - sb);
-        char *dst_line0 = a.dst + (c0 * V - ph) * ES;
-        switch (sb) {
-        case 0: flatten_full_chunks<ES, 0>(src_line0, dst_line0, t_beg, t_end); break;
-        case 4: flatten_full_chunks<ES, 4>(src_line0, dst_line0, t_beg, t_end); break;
-        case 8: flatten_full_chunks<ES, 8>(src_line0, dst_line0, t_beg, t_end); break;
-        case 12: flatten_full_chunks<ES, 12>(src_line0, dst_line0, t_beg, t_end); break;
-        default:
-            if constexpr (ES == 2) {
-                switch (sb) {
-                case 2: flatten_full_chunks<ES, 2>(src_line0, dst_line0, t_beg, t_end); break;
-                case 6: flatten_full_chunks<ES, 6>(src_line0, dst_line0, t_beg, t_end); break;
-                case 10: flatten_full_chunks<ES, 10>(src_line0, dst_line0, t_beg, t_end); break;
-                default: flatten_full_chunks<ES, 14>(src_line0, dst_line0, t_beg, t_end); break;
                 }
             }
-            break;
+        }
+        if (has_full) {
+            const uint64_t t_beg = k * kFlatTileChunks;
+            const uint64_t t_end =
+                (t_beg + kFlatTileChunks < c1 - c0) ? t_beg + kFlatTileChunks : c1 - c0;
+            // first full line's source bytes and their 16-byte phase (uniform)
+            const uintptr_t s0 = (uintptr_t)(src + (c0 * V - ph - e_lo) * ES);
+            const uint32_t sb = (uint32_t)(s0 & 15u);
+            const char *sl = (const char *)(s0 - sb);
+            char *dl = a.dst + (c0 * V - ph) * ES;
+            switch (sb) {
+            case 0: flatten_full_chunks<ES, 0, MODE>(sl, dl, t_beg, t_end, acc); break;
+            case 4: flatten_full_chunks<ES, 4, MODE>(sl, dl, t_beg, t_end, acc); break;
+            case 8: flatten_full_chunks<ES, 8, MODE>(sl, dl, t_beg, t_end, acc); break;
+            case 12: flatten_full_chunks<ES, 12, MODE>(sl, dl, t_beg, t_end, acc); break;
+            default:
+                if constexpr (ES == 2) {
+                    switch (sb) {
+                    case 2: flatten_full_chunks<ES, 2, MODE>(sl, dl, t_beg, t_end, acc); break;
+                    case 6: flatten_full_chunks<ES, 6, MODE>(sl, dl, t_beg, t_end, acc); break;
+                    case 10: flatten_full_chunks<ES, 10, MODE>(sl, dl, t_beg, t_end, acc); break;
+                    default: flatten_full_chunks<ES, 14, MODE>(sl, dl, t_beg, t_end, acc); break;
+                    }
+                }
+                break;
+            }
+        }
+        if constexpr (MODE != kCopy) {
+            const double t = block_sum(acc);
+            if (threadIdx.x == 0)
+                a.part[a.tile_base + tile] = t;
         }
     }
 }
@@ -373,37 +423,14 @@ uint64_t stats_tiles_max(uint64_t n)
     return t ? t : 1;
 }
 
-size_t stats_workspace_bytes(uint64_t n)
+// Workspace for `tiles` partials plus the second reduction level.
+size_t partials_bytes(uint64_t tiles)
 {
-    const uint64_t t = stats_tiles_max(n);
-    const uint64_t words = t + (t + kReduceGroup - 1) / kReduceGroup;
+    const uint64_t words = tiles + (tiles + kReduceGroup - 1) / kReduceGroup;
     return (size_t)((words * sizeof(double) + 15) / 16 * 16);
 }
 
-template <bool BF16>
-__device__ __forceinline__ void accum2(uint32_t w, double &acc)
-{
-    const double a = (double)to_f32<BF16>(w & 0xffffu);
-    const double b = (double)hi_to_f32<BF16>(w);
-    acc = fma(a, a, acc);  // squares of 16-bit values are exact in fp64
-    acc = fma(b, b, acc);
-}
-
-// Sum over the block in a fixed order (butterfly within waves, then waves in
-// order); the result is valid in thread 0.
-__device__ __forceinline__ double block_sum(double x)
-{
-    __shared__ double s_part[kBlock / 64];
-    x = wave_sum(x);
-    if (threadIdx.x % 64 == 0)
-        s_part[threadIdx.x / 64] = x;
-    __syncthreads();
-    double t = 0.0;
-    if (threadIdx.x == 0)
-        for (int i = 0; i < kBlock / 64; ++i)
-            t += s_part[i];
-    return t;
-}
+size_t stats_workspace_bytes(uint64_t n) { return partials_bytes(stats_tiles_max(n)); }
 
 template <bool BF16>
 __global__ void __launch_bounds__(kBlock)
@@ -687,48 +714,65 @@ inline uint32_t grid_for(uint64_t work_items, uint64_t per_block, uint32_t max_b
     return (uint32_t)b;
 }
 
-template <int ES>
+template <int ES, int MODE>
 zero_status flatten_launch(FlatArgs &a, hipStream_t stream)
 {
 #if ZERO_FLAT_ONESHOT
     const uint32_t grid = grid_for(a.tile_lo[a.n_segs], 1, 0x7ffffff0u);
 #else
-    const uint32_t grid = grid_for(a.tile_lo[a.n_segs], 1, resident_blocks(flatten_segments<ES>));
+    const uint32_t grid =
+        grid_for(a.tile_lo[a.n_segs], 1, resident_blocks(flatten_segments<ES, MODE>));
 #endif
-    hipLaunchKernelGGL(flatten_segments<ES>, dim3(grid), dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL((flatten_segments<ES, MODE>), dim3(grid), dim3(kBlock), 0, stream, a);
     return launch_status("zero_bucket_flatten");
 }
 
-}  // namespace
-
-// ============================================================== C entry points
-extern "C" zero_status zero_bucket_flatten(const void *const *tensor_ptrs, const uint64_t *numel,
-                                           uint32_t n_tensors, zero_dtype dt, uint64_t range_begin,
-                                           uint64_t count, void *dst, void *stream)
+// Upper bound of the tiles that a gather of elements [range_begin, range_end)
+// uses, over every 16-byte phase of the destination.
+uint64_t flatten_tiles_max(const uint64_t *numel, uint32_t n_tensors, uint64_t range_begin,
+                           uint64_t range_end)
 {
-    if (dt != ZERO_F32 && dt != ZERO_F16 && dt != ZERO_BF16)
-        return fail(ZERO_EINVAL, "zero_bucket_flatten: bad dtype %d", (int)dt);
+    uint64_t tiles = 0, start = 0;
+    for (uint32_t i = 0; i < n_tensors; ++i) {
+        const uint64_t lo = start > range_begin ? start : range_begin;
+        const uint64_t hi = start + numel[i] < range_end ? start + numel[i] : range_end;
+        start += numel[i];
+        if (lo >= hi)
+            continue;
+        const uint64_t full = (hi - lo) / 8;  // at most this many full 16-byte lines
+        tiles += full ? (full + kFlatTileChunks - 1) / kFlatTileChunks : 1;
+    }
+    return tiles ? tiles : 1;
+}
+
+// Shared body of the two gather entry points.  mode: kCopy or a stats mode;
+// part: per-tile partials (stats modes).  *n_tiles: tiles used.
+zero_status flatten_impl(const char *what, const void *const *tensor_ptrs, const uint64_t *numel,
+                         uint32_t n_tensors, zero_dtype dt, uint64_t range_begin, uint64_t count,
+                         void *dst, int mode, double *part, hipStream_t stream,
+                         uint64_t *n_tiles)
+{
+    *n_tiles = 0;
     if (n_tensors > 0 && (!tensor_ptrs || !numel))
-        return fail(ZERO_EINVAL, "zero_bucket_flatten: NULL tensor table");
+        return fail(ZERO_EINVAL, "%s: NULL tensor table", what);
     const uint64_t es = dt == ZERO_F32 ? 4 : 2;
     uint64_t psi = 0;
     for (uint32_t i = 0; i < n_tensors; ++i)
         if (__builtin_add_overflow(psi, numel[i], &psi))
-            return fail(ZERO_EINVAL, "zero_bucket_flatten: total size overflows");
+            return fail(ZERO_EINVAL, "%s: total size overflows", what);
     uint64_t range_end;
     if (__builtin_add_overflow(range_begin, count, &range_end) || range_end > psi)
-        return fail(ZERO_EINVAL, "zero_bucket_flatten: range [%llu, +%llu) beyond %llu elements",
+        return fail(ZERO_EINVAL, "%s: range [%llu, +%llu) beyond %llu elements", what,
                     (unsigned long long)range_begin, (unsigned long long)count,
                     (unsigned long long)psi);
     if (count == 0)
         return ZERO_OK;
     if (!dst)
-        return fail(ZERO_EINVAL, "zero_bucket_flatten: NULL dst");
+        return fail(ZERO_EINVAL, "%s: NULL dst", what);
     if (!aligned(dst, es))
-        return fail(ZERO_EALIGN, "zero_bucket_flatten: dst not %llu-byte aligned",
-                    (unsigned long long)es);
+        return fail(ZERO_EALIGN, "%s: dst not %llu-byte aligned", what, (unsigned long long)es);
     if (count > UINT64_MAX / es)
-        return fail(ZERO_EINVAL, "zero_bucket_flatten: count too large");
+        return fail(ZERO_EINVAL, "%s: count too large", what);
 
     // check every intersecting tensor before launching anything
     uint64_t start = 0;
@@ -741,16 +785,17 @@ extern "C" zero_status zero_bucket_flatten(const void *const *tensor_ptrs, const
             continue;
         const char *src = (const char *)tensor_ptrs[i];
         if (!src)
-            return fail(ZERO_EINVAL, "zero_bucket_flatten: NULL pointer for tensor %u", i);
+            return fail(ZERO_EINVAL, "%s: NULL pointer for tensor %u", what, i);
         if (!aligned(src, es))
-            return fail(ZERO_EALIGN, "zero_bucket_flatten: tensor %u not %llu-byte aligned", i,
+            return fail(ZERO_EALIGN, "%s: tensor %u not %llu-byte aligned", what, i,
                         (unsigned long long)es);
         if (overlap(src + (lo - t_lo) * es, (hi - lo) * es, dst, count * es))
-            return fail(ZERO_EINVAL, "zero_bucket_flatten: dst overlaps tensor %u", i);
+            return fail(ZERO_EINVAL, "%s: dst overlaps tensor %u", what, i);
     }
 
     FlatArgs a{};
     a.dst = (char *)dst;
+    a.part = part;
     a.dst_phase = (uint32_t)(((uintptr_t)dst & 15u) / es);
     start = 0;
     for (uint32_t i = 0; i < n_tensors; ++i) {
@@ -774,15 +819,63 @@ extern "C" zero_status zero_bucket_flatten(const void *const *tensor_ptrs, const
         a.tile_lo[s + 1] = a.tile_lo[s] + tiles;
         a.n_segs = s + 1;
         if (a.n_segs == kMaxSegs || hi == range_end) {
-            const zero_status st = es == 4 ? flatten_launch<4>(a, (hipStream_t)stream)
-                                           : flatten_launch<2>(a, (hipStream_t)stream);
+            zero_status st;
+            if (es == 4)
+                st = flatten_launch<4, kCopy>(a, stream);
+            else if (mode == kStatsF16)
+                st = flatten_launch<2, kStatsF16>(a, stream);
+            else if (mode == kStatsBF16)
+                st = flatten_launch<2, kStatsBF16>(a, stream);
+            else
+                st = flatten_launch<2, kCopy>(a, stream);
             if (st != ZERO_OK)
                 return st;
+            a.tile_base += a.tile_lo[a.n_segs];
             a.n_segs = 0;
             a.tile_lo[0] = 0;
         }
     }
+    *n_tiles = a.tile_base;
     return ZERO_OK;
+}
+
+}  // namespace
+
+namespace {
+// Fixed-order reduction of `tiles` per-tile partials (at part) into *out:
+// groups of kReduceGroup when there are many, then one block.
+zero_status reduce_partials(double *part, uint64_t tiles, double inv_scale, zero_grad_stats_t *out,
+                            hipStream_t s)
+{
+    const double *last = part;
+    uint64_t n_last = tiles;
+    if (tiles > kFinalMax) {
+        double *part2 = part + tiles;
+        const uint64_t groups = (tiles + kReduceGroup - 1) / kReduceGroup;
+        hipLaunchKernelGGL(stats_reduce, dim3((uint32_t)groups), dim3(kBlock), 0, s,
+                           (const double *)part, tiles, part2);
+        const zero_status st = launch_status("gradient statistics: reduce");
+        if (st != ZERO_OK)
+            return st;
+        last = part2;
+        n_last = groups;
+    }
+    hipLaunchKernelGGL(stats_final, dim3(1), dim3(kBlock), 0, s, last, n_last,
+                       inv_scale * inv_scale, out);
+    return launch_status("gradient statistics: final");
+}
+}  // namespace
+
+// ============================================================== C entry points
+extern "C" zero_status zero_bucket_flatten(const void *const *tensor_ptrs, const uint64_t *numel,
+                                           uint32_t n_tensors, zero_dtype dt, uint64_t range_begin,
+                                           uint64_t count, void *dst, void *stream)
+{
+    if (dt != ZERO_F32 && dt != ZERO_F16 && dt != ZERO_BF16)
+        return fail(ZERO_EINVAL, "zero_bucket_flatten: bad dtype %d", (int)dt);
+    uint64_t tiles;
+    return flatten_impl("zero_bucket_flatten", tensor_ptrs, numel, n_tensors, dt, range_begin,
+                        count, dst, kCopy, nullptr, (hipStream_t)stream, &tiles);
 }
 
 extern "C" zero_status zero_grad_stats_workspace(uint64_t n, size_t *bytes)
@@ -835,25 +928,65 @@ extern "C" zero_status zero_grad_stats(const void *grad, zero_dtype gdt, uint64_
     else
         hipLaunchKernelGGL(stats_pass1<false>, dim3((uint32_t)tiles), dim3(kBlock), 0, s, g, head,
                            nchunks, tail_beg, n, part);
-    zero_status st = launch_status("zero_grad_stats pass 1");
+    const zero_status st = launch_status("zero_grad_stats pass 1");
     if (st != ZERO_OK)
         return st;
-    const double *last = part;
-    uint64_t n_last = tiles;
-    if (tiles > kFinalMax) {
-        double *part2 = part + tiles;
-        const uint64_t groups = (tiles + kReduceGroup - 1) / kReduceGroup;
-        hipLaunchKernelGGL(stats_reduce, dim3((uint32_t)groups), dim3(kBlock), 0, s,
-                           (const double *)part, tiles, part2);
-        st = launch_status("zero_grad_stats reduce");
-        if (st != ZERO_OK)
-            return st;
-        last = part2;
-        n_last = groups;
-    }
-    hipLaunchKernelGGL(stats_final, dim3(1), dim3(kBlock), 0, s, last, n_last,
-                       inv_loss_scale * inv_loss_scale, d_stats);
-    return launch_status("zero_grad_stats final");
+    return reduce_partials(part, tiles, inv_loss_scale, d_stats, s);
+}
+
+extern "C" zero_status zero_bucket_flatten_stats_workspace(const uint64_t *numel, uint32_t n_tensors,
+                                                          uint64_t range_begin, uint64_t count,
+                                                          size_t *bytes)
+{
+    if (!bytes)
+        return fail(ZERO_EINVAL, "zero_bucket_flatten_stats_workspace: NULL output");
+    if (n_tensors > 0 && !numel)
+        return fail(ZERO_EINVAL, "zero_bucket_flatten_stats_workspace: NULL numel");
+    uint64_t range_end;
+    if (__builtin_add_overflow(range_begin, count, &range_end))
+        return fail(ZERO_EINVAL, "zero_bucket_flatten_stats_workspace: range overflows");
+    *bytes = partials_bytes(flatten_tiles_max(numel, n_tensors, range_begin, range_end));
+    return ZERO_OK;
+}
+
+extern "C" zero_status zero_bucket_flatten_stats(const void *const *tensor_ptrs,
+                                                 const uint64_t *numel, uint32_t n_tensors,
+                                                 zero_dtype gdt, uint64_t range_begin,
+                                                 uint64_t count, void *dst, double inv_loss_scale,
+                                                 void *workspace, size_t ws_bytes,
+                                                 zero_grad_stats_t *d_stats, void *stream)
+{
+    const char *what = "zero_bucket_flatten_stats";
+    if (gdt != ZERO_F16 && gdt != ZERO_BF16)
+        return fail(ZERO_EINVAL, "%s: gradient dtype must be F16 or BF16", what);
+    if (!d_stats)
+        return fail(ZERO_EINVAL, "%s: NULL d_stats", what);
+    if (!(std::isfinite(inv_loss_scale) && inv_loss_scale > 0.0))
+        return fail(ZERO_EINVAL, "%s: inv_loss_scale must be finite and > 0", what);
+    if (!workspace)
+        return fail(ZERO_EINVAL, "%s: NULL workspace", what);
+    if (n_tensors > 0 && !numel)
+        return fail(ZERO_EINVAL, "%s: NULL numel", what);
+    uint64_t range_end;
+    if (__builtin_add_overflow(range_begin, count, &range_end))
+        return fail(ZERO_EINVAL, "%s: range overflows", what);
+    const size_t need = partials_bytes(flatten_tiles_max(numel, n_tensors, range_begin, range_end));
+    if (ws_bytes < need)
+        return fail(ZERO_ENOSPC, "%s: workspace %zu bytes < %zu", what, ws_bytes, need);
+    if (!aligned(workspace, 16) || !aligned(d_stats, 8))
+        return fail(ZERO_EALIGN, "%s: misaligned workspace or d_stats", what);
+    if (overlap(workspace, ws_bytes, d_stats, sizeof *d_stats) ||
+        overlap(workspace, ws_bytes, dst, 2 * count) ||
+        overlap(d_stats, sizeof *d_stats, dst, 2 * count))
+        return fail(ZERO_EINVAL, "%s: overlapping buffers", what);
+    hipStream_t s = (hipStream_t)stream;
+    uint64_t tiles = 0;
+    const zero_status st =
+        flatten_impl(what, tensor_ptrs, numel, n_tensors, gdt, range_begin, count, dst,
+                     gdt == ZERO_BF16 ? kStatsBF16 : kStatsF16, (double *)workspace, s, &tiles);
+    if (st != ZERO_OK)
+        return st;
+    return reduce_partials((double *)workspace, tiles, inv_loss_scale, d_stats, s);
 }
 
 namespace {
