@@ -306,7 +306,7 @@ def _expected_from_sources(grads, plan, idx):
     return out
 
 
-def _run_sampled(cfg, r, idx, fill_grads, label):
+def _run_sampled(cfg, r, idx, fill_grads, label, fused=False):
     """cfg.steps steps on the full-size shard; oracle on the sampled indices
     with its own norm over every gradient."""
     idx_t = torch.from_numpy(idx).to(dev())
@@ -317,7 +317,7 @@ def _run_sampled(cfg, r, idx, fill_grads, label):
     for k in range(cfg.steps):
         fill_grads(k)
         th0, m0, v0 = (a[idx_t].cpu().numpy() for a in (r.master, r.m, r.v))
-        r.stats_and_step()
+        r.stats_and_step(fused)
         torch.cuda.synchronize()
         st = z.read_grad_stats(r.stats)
         sq, ov = _oracle_norm_streamed(r.g, cfg.dtype, cfg.hp.inv_loss_scale)
@@ -347,7 +347,10 @@ def _run_sampled(cfg, r, idx, fill_grads, label):
 
 
 @pytest.mark.timeout(900)
-def test_workload2_gpt2_1p5b_sampled():
+@pytest.mark.parametrize("fused", [True, False])
+def test_workload2_gpt2_1p5b_sampled(fused):
+    """The bench's workload and launch configuration (fused: the bench's
+    default step; unfused: one gather per 500M-element buffer, then stats)."""
     cfg = CONFIGS[2]
     r = Rank(cfg)
     assert r.n == cfg.psi == 1_557_611_200
@@ -357,11 +360,14 @@ def test_workload2_gpt2_1p5b_sampled():
 
     def fill(k):
         grads = gen.device_grad_list(cfg, k, dev())
-        r.gather(grads)
+        if fused:
+            r.gather_with_stats(grads)
+        else:
+            r.gather(grads)
         exp = _expected_from_sources(grads, plan, idx)
         assert np.array_equal(_to_host16(r.g[torch.from_numpy(idx).to(dev())]), exp), k
 
-    _run_sampled(cfg, r, idx, fill, "workload 2")
+    _run_sampled(cfg, r, idx, fill, f"workload 2 {'fused' if fused else 'unfused'}", fused)
     st = z.read_adam_state(r.state)
     assert st.coef < 0.1  # clipping at 1.0 is active on this workload
 
