@@ -48,7 +48,8 @@ typedef enum {
     ZERO_EINVAL = 1, /* an argument is out of its domain */
     ZERO_ENOSPC = 2, /* a caller-provided capacity (segments, workspace) is too small */
     ZERO_EALIGN = 3, /* a pointer is not aligned to its element size */
-    ZERO_EDEVICE = 4 /* the HIP runtime reported an error for a launch */
+    ZERO_EDEVICE = 4, /* the HIP runtime reported an error for a launch or copy */
+    ZERO_EIO = 5      /* a checkpoint file could not be created, read or written */
 } zero_status;
 
 typedef enum { ZERO_F32 = 0, ZERO_F16 = 1, ZERO_BF16 = 2 } zero_dtype;
@@ -231,6 +232,56 @@ typedef struct {
 zero_status zero_adam_step(const zero_adamw *hp, const void *grad, zero_dtype gdt, float *master,
                            float *exp_avg, float *exp_avg_sq, void *param_out, zero_dtype pdt,
                            uint64_t n, const zero_grad_stats_t *d_stats,
+                           zero_adam_state_t *d_state, void *stream);
+
+/* ------------------------------------------------------ sharded checkpoints */
+
+/* Header of one rank's checkpoint file (64 bytes, little-endian). */
+typedef struct {
+    char magic[8];     /* "ZEROCKPT" */
+    uint32_t version;  /* 1 */
+    uint32_t nd;       /* ranks of the saved run */
+    uint32_t rank;     /* this file's rank */
+    uint32_t pad;
+    uint64_t psi;      /* flat parameter count of the model */
+    uint64_t begin;    /* this rank's range [begin, end) of the flat vector */
+    uint64_t end;
+    uint64_t step;     /* device step counter when saved */
+    uint64_t reserved; /* zero */
+} zero_ckpt_header;
+
+/* ("ZeRO" AI-library tutorial page, section "Checkpoint 与恢复": with sharded
+ * checkpoints each rank writes only the state it is responsible for, and the
+ * files carry the metadata a resume needs.)  Writes rank `rank`'s optimizer
+ * state of a psi-parameter model split over nd ranks to `path`: the header,
+ * then the n = end - begin fp32 master, exp_avg and exp_avg_sq values
+ * (device arrays of the rank's shard, in that order).  The 16-bit params are
+ * not stored: they are the rounding of the master.  Synchronises `stream`
+ * first, so pending updates are included; the file appears under `path`
+ * only once complete (written to "<path>.tmp", flushed, renamed).
+ * Errors: ZERO_EINVAL (bad partition, NULL path/arrays/d_state), ZERO_EIO,
+ * ZERO_EDEVICE. */
+zero_status zero_ckpt_save(const char *path, uint64_t psi, uint32_t nd, uint32_t rank,
+                           const float *master, const float *exp_avg, const float *exp_avg_sq,
+                           const zero_adam_state_t *d_state, void *stream);
+
+/* Reads and checks the header of a checkpoint file: magic and version, a range
+ * equal to zero_partition(psi, nd, rank), and a file size that matches it.
+ * Errors: ZERO_EINVAL (not a shard, inconsistent range), ZERO_EIO. */
+zero_status zero_ckpt_read_header(const char *path, zero_ckpt_header *out);
+
+/* Restores rank `rank` of nd ranks from the n_paths shard files of one saved
+ * run, which may have used any number of ranks (re-sharding: the saved run's
+ * ranks and the new ranks partition the same flat vector differently).  The
+ * files, in any order, must be every shard of one save: the same psi and
+ * step, ranges that tile [0, psi) exactly.  Fills the device arrays master,
+ * exp_avg, exp_avg_sq (this rank's n = end - begin elements) from the files
+ * that intersect its range and sets *d_state to the saved step with the
+ * per-step scalars cleared (the next zero_adam_step recomputes them).
+ * Synchronises `stream`.  Errors: ZERO_EINVAL (wrong psi, files from
+ * different saves, gaps or overlaps, bad partition), ZERO_EIO, ZERO_EDEVICE. */
+zero_status zero_ckpt_load(const char *const *paths, uint32_t n_paths, uint64_t psi, uint32_t nd,
+                           uint32_t rank, float *master, float *exp_avg, float *exp_avg_sq,
                            zero_adam_state_t *d_state, void *stream);
 
 #ifdef __cplusplus

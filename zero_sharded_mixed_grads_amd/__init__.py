@@ -17,7 +17,7 @@ import torch  # loads the HIP runtime that the library then binds to
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libzero_mi355x.so")
 
-ZERO_OK, ZERO_EINVAL, ZERO_ENOSPC, ZERO_EALIGN, ZERO_EDEVICE = range(5)
+ZERO_OK, ZERO_EINVAL, ZERO_ENOSPC, ZERO_EALIGN, ZERO_EDEVICE, ZERO_EIO = range(6)
 ZERO_F32, ZERO_F16, ZERO_BF16 = range(3)
 
 _DTYPES = {"f32": ZERO_F32, "f16": ZERO_F16, "bf16": ZERO_BF16,
@@ -55,12 +55,19 @@ class AdamState(ctypes.Structure):  # zero_adam_state_t, device resident
                 ("decay", ctypes.c_float), ("pad1", U32)]
 
 
+class CkptHeader(ctypes.Structure):  # zero_ckpt_header
+    _fields_ = [("magic", ctypes.c_char * 8), ("version", U32), ("nd", U32), ("rank", U32),
+                ("pad", U32), ("psi", U64), ("begin", U64), ("end", U64), ("step", U64),
+                ("reserved", U64)]
+
+
 assert ctypes.sizeof(GradStats) == 16 and ctypes.sizeof(AdamState) == 64
+assert ctypes.sizeof(CkptHeader) == 64
 
 EXPORTS = ("zero_status_str", "zero_last_error", "zero_partition", "zero_mem_bytes",
            "zero_bucket_plan", "zero_bucket_flatten", "zero_grad_stats_workspace",
            "zero_grad_stats", "zero_bucket_flatten_stats_workspace", "zero_bucket_flatten_stats",
-           "zero_adam_step")
+           "zero_adam_step", "zero_ckpt_save", "zero_ckpt_read_header", "zero_ckpt_load")
 
 _lib = None
 
@@ -92,6 +99,10 @@ def lib():
                                                 ctypes.c_size_t, VP, VP]
         L.zero_adam_step.argtypes = [ctypes.POINTER(AdamW), VP, ctypes.c_int, VP, VP, VP, VP,
                                      ctypes.c_int, U64, VP, VP, VP]
+        L.zero_ckpt_save.argtypes = [ctypes.c_char_p, U64, U32, U32, VP, VP, VP, VP, VP]
+        L.zero_ckpt_read_header.argtypes = [ctypes.c_char_p, ctypes.POINTER(CkptHeader)]
+        L.zero_ckpt_load.argtypes = [ctypes.POINTER(ctypes.c_char_p), U32, U64, U32, U32, VP, VP,
+                                     VP, VP, VP]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -208,6 +219,26 @@ def zero_adam_step(hp: AdamW, grad, gdtype, master, exp_avg, exp_avg_sq, param_o
     _check(lib().zero_adam_step(ctypes.byref(hp), _ptr(grad), _dtype(gdtype), _ptr(master),
                                 _ptr(exp_avg), _ptr(exp_avg_sq), _ptr(param_out), _dtype(pdtype),
                                 n, _ptr(d_stats), _ptr(d_state), _stream(stream)))
+
+
+# ---------------------------------------------------- sharded checkpoints
+def zero_ckpt_save(path: str, psi: int, nd: int, rank: int, master, exp_avg, exp_avg_sq,
+                   d_state, stream=None) -> None:
+    _check(lib().zero_ckpt_save(os.fsencode(path), psi, nd, rank, _ptr(master), _ptr(exp_avg),
+                                _ptr(exp_avg_sq), _ptr(d_state), _stream(stream)))
+
+
+def zero_ckpt_read_header(path: str) -> CkptHeader:
+    h = CkptHeader()
+    _check(lib().zero_ckpt_read_header(os.fsencode(path), ctypes.byref(h)))
+    return h
+
+
+def zero_ckpt_load(paths: Sequence[str], psi: int, nd: int, rank: int, master, exp_avg,
+                   exp_avg_sq, d_state, stream=None) -> None:
+    arr = (ctypes.c_char_p * len(paths))(*[os.fsencode(p) for p in paths])
+    _check(lib().zero_ckpt_load(arr, len(paths), psi, nd, rank, _ptr(master), _ptr(exp_avg),
+                                _ptr(exp_avg_sq), _ptr(d_state), _stream(stream)))
 
 
 # ----------------------------------------------- device struct conveniences

@@ -22,7 +22,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}", f"-I
 DEVICE = [f"--offload-arch={ARCH}", "-mcode-object-version=5", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-fno-gpu-flush-denormals-to-zero", "-Wno-unused-command-line-argument"]
 
-SOURCES = ["zero_host.cpp", "zero_kernels.hip"]
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HOST = [f"-I{ROCM}/include", "-D__HIP_PLATFORM_AMD__=1"]  # HIP runtime API from host C++
+
+SOURCES = ["zero_host.cpp", "zero_ckpt.cpp", "zero_kernels.hip"]
 
 
 def _run(cmd):
@@ -40,7 +43,7 @@ def build(verbose: bool = True) -> str:
         if src.endswith(".hip"):
             _run([HIPCC, *COMMON, *DEVICE, "-x", "hip", "-c", path, "-o", obj])
         else:
-            _run([HIPCC, *COMMON, "-x", "c++", "-c", path, "-o", obj])
+            _run([HIPCC, *COMMON, *HOST, "-x", "c++", "-c", path, "-o", obj])
         objs.append(obj)
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])

@@ -1,0 +1,249 @@
+// Sharded checkpoints of one rank's optimizer state ("ZeRO" AI-library
+// tutorial page, section "Checkpoint 与恢复": each rank writes only the state
+// it owns; resuming may need a different number of GPUs).
+//
+// File layout (little-endian): a 64-byte zero_ckpt_header, then the rank's
+// fp32 master, momentum and variance, n = end - begin elements each.  Save
+// writes to "<path>.tmp", flushes it to storage and renames it over <path>,
+// so a crash never leaves a half-written file under the final name.  Load
+// takes the shard files of a saved run with any number of ranks, checks that
+// they describe one run (same psi and step, ranges tiling [0, psi)), and
+// copies the intersection of each file with the loading rank's range.
+#include <hip/hip_runtime_api.h>
+
+#include <fcntl.h>
+#include <sys/stat.h>
+#include <unistd.h>
+
+#include <algorithm>
+#include <cerrno>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "zero_internal.h"
+
+using zero::fail;
+
+namespace {
+
+constexpr char kMagic[8] = {'Z', 'E', 'R', 'O', 'C', 'K', 'P', 'T'};
+constexpr uint32_t kVersion = 1;
+constexpr uint64_t kChunk = 64ull << 20;  // bytes staged through host memory at a time
+
+static_assert(sizeof(zero_ckpt_header) == 64, "checkpoint header is 64 bytes");
+
+struct Fd {
+    int fd = -1;
+    ~Fd() { if (fd >= 0) close(fd); }
+};
+
+bool write_all(int fd, const void *buf, size_t len)
+{
+    const char *p = (const char *)buf;
+    while (len) {
+        const ssize_t k = write(fd, p, len);
+        if (k < 0 && errno == EINTR)
+            continue;
+        if (k <= 0)
+            return false;
+        p += k;
+        len -= (size_t)k;
+    }
+    return true;
+}
+
+bool read_at(int fd, void *buf, size_t len, uint64_t off)
+{
+    char *p = (char *)buf;
+    while (len) {
+        const ssize_t k = pread(fd, p, len, (off_t)off);
+        if (k < 0 && errno == EINTR)
+            continue;
+        if (k <= 0)
+            return false;
+        p += k;
+        off += (uint64_t)k;
+        len -= (size_t)k;
+    }
+    return true;
+}
+
+zero_status hip_check(hipError_t e, const char *what)
+{
+    if (e != hipSuccess)
+        return fail(ZERO_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+    return ZERO_OK;
+}
+
+}  // namespace
+
+extern "C" zero_status zero_ckpt_save(const char *path, uint64_t psi, uint32_t nd, uint32_t rank,
+                                      const float *master, const float *exp_avg,
+                                      const float *exp_avg_sq, const zero_adam_state_t *d_state,
+                                      void *stream)
+{
+    if (!path || !d_state)
+        return fail(ZERO_EINVAL, "zero_ckpt_save: NULL path or d_state");
+    uint64_t begin, end;
+    zero_status st = zero_partition(psi, nd, rank, &begin, &end);
+    if (st != ZERO_OK)
+        return st;
+    const uint64_t n = end - begin;
+    if (n > 0 && (!master || !exp_avg || !exp_avg_sq))
+        return fail(ZERO_EINVAL, "zero_ckpt_save: NULL state array with n > 0");
+    hipStream_t s = (hipStream_t)stream;
+    zero_adam_state_t state;
+    if ((st = hip_check(hipMemcpyAsync(&state, d_state, sizeof state, hipMemcpyDeviceToHost, s),
+                        "zero_ckpt_save: reading the step state")) != ZERO_OK ||
+        (st = hip_check(hipStreamSynchronize(s), "zero_ckpt_save: stream")) != ZERO_OK)
+        return st;
+
+    zero_ckpt_header h{};
+    std::memcpy(h.magic, kMagic, sizeof kMagic);
+    h.version = kVersion;
+    h.nd = nd;
+    h.rank = rank;
+    h.psi = psi;
+    h.begin = begin;
+    h.end = end;
+    h.step = state.step;
+
+    const std::string tmp = std::string(path) + ".tmp";
+    Fd f;
+    f.fd = open(tmp.c_str(), O_WRONLY | O_CREAT | O_TRUNC, 0644);
+    if (f.fd < 0)
+        return fail(ZERO_EIO, "zero_ckpt_save: cannot create %s: %s", tmp.c_str(), strerror(errno));
+    if (!write_all(f.fd, &h, sizeof h))
+        return fail(ZERO_EIO, "zero_ckpt_save: writing %s: %s", tmp.c_str(), strerror(errno));
+    std::vector<char> buf((size_t)std::min<uint64_t>(kChunk, std::max<uint64_t>(4 * n, 1)));
+    for (const float *arr : {master, exp_avg, exp_avg_sq}) {
+        for (uint64_t off = 0; off < 4 * n; off += buf.size()) {
+            const size_t len = (size_t)std::min<uint64_t>(buf.size(), 4 * n - off);
+            if ((st = hip_check(hipMemcpyAsync(buf.data(), (const char *)arr + off, len,
+                                               hipMemcpyDeviceToHost, s),
+                                "zero_ckpt_save: copy to host")) != ZERO_OK ||
+                (st = hip_check(hipStreamSynchronize(s), "zero_ckpt_save: stream")) != ZERO_OK)
+                return st;
+            if (!write_all(f.fd, buf.data(), len))
+                return fail(ZERO_EIO, "zero_ckpt_save: writing %s: %s", tmp.c_str(),
+                            strerror(errno));
+        }
+    }
+    if (fsync(f.fd) != 0)
+        return fail(ZERO_EIO, "zero_ckpt_save: fsync %s: %s", tmp.c_str(), strerror(errno));
+    close(f.fd);
+    f.fd = -1;
+    if (rename(tmp.c_str(), path) != 0)
+        return fail(ZERO_EIO, "zero_ckpt_save: rename to %s: %s", path, strerror(errno));
+    return ZERO_OK;
+}
+
+extern "C" zero_status zero_ckpt_read_header(const char *path, zero_ckpt_header *out)
+{
+    if (!path || !out)
+        return fail(ZERO_EINVAL, "zero_ckpt_read_header: NULL argument");
+    Fd f;
+    f.fd = open(path, O_RDONLY);
+    if (f.fd < 0)
+        return fail(ZERO_EIO, "zero_ckpt_read_header: cannot open %s: %s", path, strerror(errno));
+    zero_ckpt_header h;
+    if (!read_at(f.fd, &h, sizeof h, 0))
+        return fail(ZERO_EIO, "zero_ckpt_read_header: %s is shorter than a header", path);
+    if (std::memcmp(h.magic, kMagic, sizeof kMagic) != 0 || h.version != kVersion)
+        return fail(ZERO_EINVAL, "zero_ckpt_read_header: %s is not a version-%u shard", path,
+                    kVersion);
+    uint64_t b, e;
+    if (zero_partition(h.psi, h.nd, h.rank, &b, &e) != ZERO_OK || b != h.begin || e != h.end)
+        return fail(ZERO_EINVAL, "zero_ckpt_read_header: %s: range [%llu, %llu) is not rank %u of %u",
+                    path, (unsigned long long)h.begin, (unsigned long long)h.end, h.rank, h.nd);
+    struct stat sb;
+    if (fstat(f.fd, &sb) != 0 ||
+        (uint64_t)sb.st_size != sizeof h + 12 * (h.end - h.begin))
+        return fail(ZERO_EIO, "zero_ckpt_read_header: %s has the wrong size", path);
+    *out = h;
+    return ZERO_OK;
+}
+
+extern "C" zero_status zero_ckpt_load(const char *const *paths, uint32_t n_paths, uint64_t psi,
+                                      uint32_t nd, uint32_t rank, float *master, float *exp_avg,
+                                      float *exp_avg_sq, zero_adam_state_t *d_state, void *stream)
+{
+    if (!paths || n_paths == 0 || !d_state)
+        return fail(ZERO_EINVAL, "zero_ckpt_load: no shard files or NULL d_state");
+    uint64_t begin, end;
+    zero_status st = zero_partition(psi, nd, rank, &begin, &end);
+    if (st != ZERO_OK)
+        return st;
+    const uint64_t n = end - begin;
+    if (n > 0 && (!master || !exp_avg || !exp_avg_sq))
+        return fail(ZERO_EINVAL, "zero_ckpt_load: NULL state array with n > 0");
+
+    // the files must be the complete set of shards of one saved run
+    std::vector<zero_ckpt_header> hs(n_paths);
+    for (uint32_t i = 0; i < n_paths; ++i) {
+        if (!paths[i])
+            return fail(ZERO_EINVAL, "zero_ckpt_load: NULL path %u", i);
+        if ((st = zero_ckpt_read_header(paths[i], &hs[i])) != ZERO_OK)
+            return st;
+        if (hs[i].psi != psi)
+            return fail(ZERO_EINVAL, "zero_ckpt_load: %s holds psi %llu, not %llu", paths[i],
+                        (unsigned long long)hs[i].psi, (unsigned long long)psi);
+        if (hs[i].step != hs[0].step || hs[i].nd != hs[0].nd)
+            return fail(ZERO_EINVAL, "zero_ckpt_load: %s is from another save (step or rank count)",
+                        paths[i]);
+    }
+    std::vector<uint32_t> order(n_paths);
+    for (uint32_t i = 0; i < n_paths; ++i)
+        order[i] = i;
+    std::sort(order.begin(), order.end(),
+              [&](uint32_t a, uint32_t b) { return hs[a].begin < hs[b].begin; });
+    uint64_t covered = 0;
+    for (uint32_t i : order) {
+        if (hs[i].begin != covered)
+            return fail(ZERO_EINVAL, "zero_ckpt_load: the shard files do not tile [0, %llu): "
+                        "gap or overlap at %llu", (unsigned long long)psi,
+                        (unsigned long long)covered);
+        covered = hs[i].end;
+    }
+    if (covered != psi || n_paths != hs[0].nd)
+        return fail(ZERO_EINVAL, "zero_ckpt_load: %u shard files do not cover all %u ranks",
+                    n_paths, hs[0].nd);
+
+    hipStream_t s = (hipStream_t)stream;
+    if ((st = hip_check(hipStreamSynchronize(s), "zero_ckpt_load: stream")) != ZERO_OK)
+        return st;
+    std::vector<char> buf((size_t)std::min<uint64_t>(kChunk, std::max<uint64_t>(4 * n, 1)));
+    for (uint32_t i : order) {
+        const uint64_t lo = std::max(begin, hs[i].begin), hi = std::min(end, hs[i].end);
+        if (lo >= hi)
+            continue;
+        Fd f;
+        f.fd = open(paths[i], O_RDONLY);
+        if (f.fd < 0)
+            return fail(ZERO_EIO, "zero_ckpt_load: cannot open %s: %s", paths[i], strerror(errno));
+        const uint64_t file_n = hs[i].end - hs[i].begin;
+        float *dsts[3] = {master, exp_avg, exp_avg_sq};
+        for (int a = 0; a < 3; ++a) {
+            const uint64_t src0 = sizeof(zero_ckpt_header) + 4 * (a * file_n + (lo - hs[i].begin));
+            char *dst0 = (char *)dsts[a] + 4 * (lo - begin);
+            for (uint64_t off = 0; off < 4 * (hi - lo); off += buf.size()) {
+                const size_t len = (size_t)std::min<uint64_t>(buf.size(), 4 * (hi - lo) - off);
+                if (!read_at(f.fd, buf.data(), len, src0 + off))
+                    return fail(ZERO_EIO, "zero_ckpt_load: reading %s", paths[i]);
+                if ((st = hip_check(hipMemcpyAsync(dst0 + off, buf.data(), len,
+                                                   hipMemcpyHostToDevice, s),
+                                    "zero_ckpt_load: copy to device")) != ZERO_OK ||
+                    (st = hip_check(hipStreamSynchronize(s), "zero_ckpt_load: stream")) != ZERO_OK)
+                    return st;
+            }
+        }
+    }
+    // step counter restored; the per-step scalars are recomputed by the next step
+    zero_adam_state_t state{};
+    state.step = hs[0].step;
+    if ((st = hip_check(hipMemcpyAsync(d_state, &state, sizeof state, hipMemcpyHostToDevice, s),
+                        "zero_ckpt_load: writing the step state")) != ZERO_OK)
+        return st;
+    return hip_check(hipStreamSynchronize(s), "zero_ckpt_load: stream");
+}

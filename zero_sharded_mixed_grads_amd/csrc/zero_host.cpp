@@ -39,6 +39,7 @@ extern "C" const char *zero_status_str(zero_status s)
     case ZERO_ENOSPC: return "ZERO_ENOSPC";
     case ZERO_EALIGN: return "ZERO_EALIGN";
     case ZERO_EDEVICE: return "ZERO_EDEVICE";
+    case ZERO_EIO: return "ZERO_EIO";
     }
     return "ZERO_UNKNOWN";
 }
