@@ -197,6 +197,61 @@ def copy_probe(steps: int):
     print(json.dumps({"copy_probe": res}), flush=True)
 
 
+def offload_bench(cfg_idx: int, steps: int, warmup: int, chunk: int = 1 << 24):
+    """The optimizer step with master/m/v in host memory (zero_offload_adam_step)
+    on the same shard: gradients and params on the device, statistics on the
+    device, AdamW on the host cores.  Prints one JSON line."""
+    import torch
+    import zero_sharded_mixed_grads_amd as z
+    from synth import CONFIGS, gen
+    cfg = CONFIGS[cfg_idx]
+    dev = torch.device("cuda:0")
+    b, e = z.zero_partition(cfg.psi, cfg.nd, cfg.rank)
+    n = e - b
+    g = torch.empty(n, dtype=gen.torch_dtype(cfg.dtype), device=dev)
+    gen.device_fill_normal_(g, cfg.grad_seed(0), cfg.grad_sigma, cfg.loss_scale)
+    p = torch.empty_like(g)
+    dm = torch.empty(n, dtype=torch.float32, device=dev)
+    gen.device_fill_normal_(dm, cfg.master_seed(), cfg.master_sigma)
+    master = dm.cpu()
+    del dm
+    m, v = torch.zeros(n), torch.zeros(n)
+    stats, state = z.new_grad_stats(dev), z.new_adam_state(dev)
+    ws = z.new_workspace(n, dev)
+    nb = z.zero_offload_staging_bytes(chunk)
+    stg = torch.empty(nb, dtype=torch.uint8, pin_memory=True)
+    hp = z.adamw(**cfg.hp.__dict__)
+    log(f"[bench] offload: n={n}, state {12 * n / 1e9:.1f} GB in host memory, "
+        f"chunks of {chunk} elements")
+
+    def step():
+        z.zero_grad_stats(g, cfg.dtype, n, cfg.hp.inv_loss_scale, ws, ws.numel(), stats)
+        z.zero_offload_adam_step(hp, g, cfg.dtype, master, m, v, p, cfg.dtype, n, stats, state,
+                                 stg, nb)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    st = z.read_adam_state(state)
+    if st.step != warmup + steps:
+        print("bench: offloaded steps were skipped; the measurement is invalid", file=sys.stderr)
+        sys.exit(3)
+    cpu = next((l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
+                if l.startswith("model name")), "unknown")
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    print(json.dumps({"offload": {
+        "workload": cfg.name + f"-nd{cfg.nd}-rank{cfg.rank}", "shard_params": n,
+        "steps": steps, "warmup": warmup, "ms_per_step": ms, "params_per_s": n / (ms * 1e-3),
+        "pcie_GB/s": 4 * n / (ms * 1e-3) / 1e9,
+        "host_state_GB/s": 24 * n / (ms * 1e-3) / 1e9,
+        "chunk_elems": chunk, "host_threads": threads, "host_cpu": cpu}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -208,6 +263,8 @@ def main():
                     help="time plain device copies of a known size instead")
     ap.add_argument("--unfused", action="store_true",
                     help="gather per fused buffer, then a separate statistics pass")
+    ap.add_argument("--offload", action="store_true",
+                    help="time the step with the optimizer state in host memory instead")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one data-parallel rank's shard on one GPU; runs on more "
@@ -216,6 +273,9 @@ def main():
 
     if args.copy_probe:
         copy_probe(args.steps)
+        return
+    if args.offload:
+        offload_bench(args.config, args.steps, args.warmup)
         return
 
     import torch

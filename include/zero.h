@@ -234,6 +234,37 @@ zero_status zero_adam_step(const zero_adamw *hp, const void *grad, zero_dtype gd
                            uint64_t n, const zero_grad_stats_t *d_stats,
                            zero_adam_state_t *d_state, void *stream);
 
+/* --------------------------------------------- optimizer state in host memory */
+
+/* Bytes of pinned host staging that zero_offload_adam_step needs to move
+ * chunk_elems gradients and parameters per chunk (two slots; chunk_elems >=
+ * 4096). */
+zero_status zero_offload_staging_bytes(uint64_t chunk_elems, size_t *bytes);
+
+/* ("ZeRO" AI-library tutorial page, section "ZeRO-Offload 与 ZeRO-Infinity":
+ * optimizer state moved to CPU memory to lift the GPU memory limit, at the
+ * cost of PCIe transfers; "ZeRO optimization" glossary page, section
+ * "Как работает": offloading to CPU memory.)  The same update as
+ * zero_adam_step, with the fp32 master, exp_avg and exp_avg_sq in HOST memory
+ * (n elements each, updated in place by host threads) while the 16-bit grad
+ * and param_out stay on the device.  The step state d_state and the optional
+ * statistics d_stats are device-resident, as for zero_adam_step, and the
+ * skip, clip and bias corrections are computed the same way.  The gradients
+ * travel device -> host and the new 16-bit params host -> device in chunks
+ * of staging_bytes / 8 elements through `staging`, caller-owned pinned host
+ * memory (e.g. from hipHostMalloc), two slots deep so that transfers overlap
+ * the host update.  The host loop performs the device kernel's fp32
+ * operations in the same order.  Synchronous: returns after the params have
+ * reached the device (or at once when the step is skipped).
+ * Errors: as zero_adam_step; ZERO_ENOSPC if staging holds fewer than 4096
+ * elements per slot. */
+zero_status zero_offload_adam_step(const zero_adamw *hp, const void *grad, zero_dtype gdt,
+                                   float *master_host, float *exp_avg_host,
+                                   float *exp_avg_sq_host, void *param_out, zero_dtype pdt,
+                                   uint64_t n, const zero_grad_stats_t *d_stats,
+                                   zero_adam_state_t *d_state, void *staging,
+                                   size_t staging_bytes, void *stream);
+
 /* ------------------------------------------------------ sharded checkpoints */
 
 /* Header of one rank's checkpoint file (64 bytes, little-endian). */

@@ -23,7 +23,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     assert set(names) == set(z.EXPORTS)
     L = ctypes.CDLL(z.LIB_PATH)
     for name in names:
@@ -240,3 +240,23 @@ def test_flatten_stats_workspace_bound():
     got = z.zero_bucket_flatten_stats_workspace(numel, 0, sum(numel))
     tiles = sum(max(1, -(-(k // 8) // 256)) for k in numel)
     assert got >= 8 * tiles
+
+
+def test_offload_validation_on_host():
+    """Rejected before any device access."""
+    n = 1 << 16
+    h = [FAKE + (i << 24) for i in range(3)]
+    g, p, stg = FAKE + (8 << 24), FAKE + (9 << 24), FAKE + (10 << 24)
+    st = FAKE + (11 << 24)
+    nb = z.zero_offload_staging_bytes(4096)
+    assert nb == 4096 * 8
+    call = z.zero_offload_adam_step
+    assert _status(call, z.adamw(), g, "f16", *h, p, "f16", n, None, None, stg, nb, 0) == z.ZERO_EINVAL
+    assert _status(call, z.adamw(lr=-1), g, "f16", *h, p, "f16", n, None, st, stg, nb, 0) == z.ZERO_EINVAL
+    assert _status(call, z.adamw(), g, "f32", *h, p, "f16", n, None, st, stg, nb, 0) == z.ZERO_EINVAL
+    assert _status(call, z.adamw(), g, "f16", *h, p, "f16", n, None, st, stg, nb - 1, 0) == z.ZERO_ENOSPC
+    assert _status(call, z.adamw(), g + 1, "f16", *h, p, "f16", n, None, st, stg, nb, 0) == z.ZERO_EALIGN
+    assert _status(call, z.adamw(), g, "f16", h[0] + 2, h[1], h[2], p, "f16", n, None, st, stg, nb,
+                   0) == z.ZERO_EALIGN
+    assert _status(call, z.adamw(), g, "f16", h[0], h[0] + 4, h[2], p, "f16", n, None, st, stg, nb,
+                   0) == z.ZERO_EINVAL

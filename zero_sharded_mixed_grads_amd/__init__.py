@@ -67,7 +67,8 @@ assert ctypes.sizeof(CkptHeader) == 64
 EXPORTS = ("zero_status_str", "zero_last_error", "zero_partition", "zero_mem_bytes",
            "zero_bucket_plan", "zero_bucket_flatten", "zero_grad_stats_workspace",
            "zero_grad_stats", "zero_bucket_flatten_stats_workspace", "zero_bucket_flatten_stats",
-           "zero_adam_step", "zero_ckpt_save", "zero_ckpt_read_header", "zero_ckpt_load")
+           "zero_adam_step", "zero_offload_staging_bytes", "zero_offload_adam_step",
+           "zero_ckpt_save", "zero_ckpt_read_header", "zero_ckpt_load")
 
 _lib = None
 
@@ -99,6 +100,10 @@ def lib():
                                                 ctypes.c_size_t, VP, VP]
         L.zero_adam_step.argtypes = [ctypes.POINTER(AdamW), VP, ctypes.c_int, VP, VP, VP, VP,
                                      ctypes.c_int, U64, VP, VP, VP]
+        L.zero_offload_staging_bytes.argtypes = [U64, ctypes.POINTER(ctypes.c_size_t)]
+        L.zero_offload_adam_step.argtypes = [ctypes.POINTER(AdamW), VP, ctypes.c_int, VP, VP,
+                                             VP, VP, ctypes.c_int, U64, VP, VP, VP,
+                                             ctypes.c_size_t, VP]
         L.zero_ckpt_save.argtypes = [ctypes.c_char_p, U64, U32, U32, VP, VP, VP, VP, VP]
         L.zero_ckpt_read_header.argtypes = [ctypes.c_char_p, ctypes.POINTER(CkptHeader)]
         L.zero_ckpt_load.argtypes = [ctypes.POINTER(ctypes.c_char_p), U32, U64, U32, U32, VP, VP,
@@ -219,6 +224,25 @@ def zero_adam_step(hp: AdamW, grad, gdtype, master, exp_avg, exp_avg_sq, param_o
     _check(lib().zero_adam_step(ctypes.byref(hp), _ptr(grad), _dtype(gdtype), _ptr(master),
                                 _ptr(exp_avg), _ptr(exp_avg_sq), _ptr(param_out), _dtype(pdtype),
                                 n, _ptr(d_stats), _ptr(d_state), _stream(stream)))
+
+
+# ------------------------------------------ optimizer state in host memory
+def zero_offload_staging_bytes(chunk_elems: int) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().zero_offload_staging_bytes(chunk_elems, ctypes.byref(out)))
+    return out.value
+
+
+def zero_offload_adam_step(hp: AdamW, grad, gdtype, master_host, exp_avg_host, exp_avg_sq_host,
+                           param_out, pdtype, n: int, d_stats, d_state, staging,
+                           staging_bytes: int, stream=None) -> None:
+    """master/exp_avg/exp_avg_sq: host tensors (or addresses); staging: pinned
+    host memory; grad, param_out, d_stats, d_state: device."""
+    _check(lib().zero_offload_adam_step(ctypes.byref(hp), _ptr(grad), _dtype(gdtype),
+                                        _ptr(master_host), _ptr(exp_avg_host),
+                                        _ptr(exp_avg_sq_host), _ptr(param_out), _dtype(pdtype),
+                                        n, _ptr(d_stats), _ptr(d_state), _ptr(staging),
+                                        staging_bytes, _stream(stream)))
 
 
 # ---------------------------------------------------- sharded checkpoints

@@ -25,7 +25,11 @@ DEVICE = [f"--offload-arch={ARCH}", "-mcode-object-version=5", "-Xclang", "-targ
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HOST = [f"-I{ROCM}/include", "-D__HIP_PLATFORM_AMD__=1"]  # HIP runtime API from host C++
 
-SOURCES = ["zero_host.cpp", "zero_ckpt.cpp", "zero_kernels.hip"]
+SOURCES = ["zero_host.cpp", "zero_ckpt.cpp", "zero_offload.cpp", "zero_kernels.hip"]
+# the host AdamW of the offload path: OpenMP threads, vectorisable sqrt, and the
+# exact operation sequence of the device kernel (no contraction)
+EXTRA = {"zero_offload.cpp": ["-fopenmp", "-fno-math-errno", "-ffp-contract=off"]}
+LINK = ["-fopenmp", f"-Wl,-rpath,{ROCM}/lib/llvm/lib"]
 
 
 def _run(cmd):
@@ -43,10 +47,11 @@ def build(verbose: bool = True) -> str:
         if src.endswith(".hip"):
             _run([HIPCC, *COMMON, *DEVICE, "-x", "hip", "-c", path, "-o", obj])
         else:
-            _run([HIPCC, *COMMON, *HOST, "-x", "c++", "-c", path, "-o", obj])
+            _run([HIPCC, *COMMON, *HOST, *EXTRA.get(src, []), "-x", "c++", "-c", path, "-o",
+                  obj])
         objs.append(obj)
     tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, *LINK, "-o", tmp])
     os.replace(tmp, LIB)
     return LIB
 

@@ -8,6 +8,7 @@
 // (AI-library tutorial page), sections ZeRO-1/2/3.
 #include "zero_internal.h"
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 
@@ -25,6 +26,23 @@ zero_status fail(zero_status s, const char *fmt, ...)
     std::vsnprintf(g_last_error + k, sizeof g_last_error - k, fmt, ap);
     va_end(ap);
     return s;
+}
+
+zero_status check_adamw(const zero_adamw &hp, const char *what)
+{
+    if (!(hp.lr >= 0.0 && std::isfinite(hp.lr)))
+        return fail(ZERO_EINVAL, "%s: lr must be finite and >= 0", what);
+    if (!(hp.beta1 >= 0.0 && hp.beta1 < 1.0) || !(hp.beta2 >= 0.0 && hp.beta2 < 1.0))
+        return fail(ZERO_EINVAL, "%s: betas must be in [0, 1)", what);
+    if (!(hp.eps > 0.0 && std::isfinite(hp.eps)))
+        return fail(ZERO_EINVAL, "%s: eps must be finite and > 0", what);
+    if (!(hp.weight_decay >= 0.0 && std::isfinite(hp.weight_decay)))
+        return fail(ZERO_EINVAL, "%s: weight_decay must be finite and >= 0", what);
+    if (!(std::isfinite(hp.inv_loss_scale) && hp.inv_loss_scale > 0.0))
+        return fail(ZERO_EINVAL, "%s: inv_loss_scale must be finite and > 0", what);
+    if (std::isnan(hp.max_grad_norm))
+        return fail(ZERO_EINVAL, "%s: max_grad_norm is NaN", what);
+    return ZERO_OK;
 }
 
 }  // namespace zero

@@ -866,6 +866,14 @@ zero_status reduce_partials(double *part, uint64_t tiles, double inv_scale, zero
 }
 }  // namespace
 
+zero_status zero::launch_adam_scalars(const zero_adamw &hp, const zero_grad_stats_t *d_stats,
+                                      zero_adam_state_t *d_state, void *stream)
+{
+    hipLaunchKernelGGL(adam_scalars, dim3(1), dim3(64), 0, (hipStream_t)stream, hp, d_stats,
+                       d_state);
+    return launch_status("adam step scalars");
+}
+
 // ============================================================== C entry points
 extern "C" zero_status zero_bucket_flatten(const void *const *tensor_ptrs, const uint64_t *numel,
                                            uint32_t n_tensors, zero_dtype dt, uint64_t range_begin,
@@ -1032,18 +1040,8 @@ extern "C" zero_status zero_adam_step(const zero_adamw *hp, const void *grad, ze
         return fail(ZERO_EINVAL, "zero_adam_step: NULL d_state");
     if ((gdt != ZERO_F16 && gdt != ZERO_BF16) || (pdt != ZERO_F16 && pdt != ZERO_BF16))
         return fail(ZERO_EINVAL, "zero_adam_step: grad and param dtypes must be F16 or BF16");
-    if (!(hp->lr >= 0.0 && std::isfinite(hp->lr)))
-        return fail(ZERO_EINVAL, "zero_adam_step: lr must be finite and >= 0");
-    if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0))
-        return fail(ZERO_EINVAL, "zero_adam_step: betas must be in [0, 1)");
-    if (!(hp->eps > 0.0 && std::isfinite(hp->eps)))
-        return fail(ZERO_EINVAL, "zero_adam_step: eps must be finite and > 0");
-    if (!(hp->weight_decay >= 0.0 && std::isfinite(hp->weight_decay)))
-        return fail(ZERO_EINVAL, "zero_adam_step: weight_decay must be finite and >= 0");
-    if (!(std::isfinite(hp->inv_loss_scale) && hp->inv_loss_scale > 0.0))
-        return fail(ZERO_EINVAL, "zero_adam_step: inv_loss_scale must be finite and > 0");
-    if (std::isnan(hp->max_grad_norm))
-        return fail(ZERO_EINVAL, "zero_adam_step: max_grad_norm is NaN");
+    if (zero_status hs = zero::check_adamw(*hp, "zero_adam_step"); hs != ZERO_OK)
+        return hs;
     if (n > 0 && (!grad || !master || !exp_avg || !exp_avg_sq || !param_out))
         return fail(ZERO_EINVAL, "zero_adam_step: NULL array with n > 0");
     if (n > UINT64_MAX / 4)
@@ -1062,8 +1060,7 @@ extern "C" zero_status zero_adam_step(const zero_adamw *hp, const void *grad, ze
                     return fail(ZERO_EINVAL, "zero_adam_step: buffers %d and %d overlap", i, j);
     }
     hipStream_t s = (hipStream_t)stream;
-    hipLaunchKernelGGL(adam_scalars, dim3(1), dim3(64), 0, s, *hp, d_stats, d_state);
-    zero_status st = launch_status("zero_adam_step scalars");
+    zero_status st = zero::launch_adam_scalars(*hp, d_stats, d_state, stream);
     if (st != ZERO_OK || n == 0)
         return st;
 
