@@ -240,6 +240,49 @@ def test_adam_without_stats_never_clips_or_skips():
     assert sa.step == 1 and sa.coef == 1.0
 
 
+_DEGENERATE = {
+    "beta1_0": dict(beta1=0.0),
+    "beta2_0": dict(beta2=0.0),
+    "betas_0": dict(beta1=0.0, beta2=0.0),
+    "no_decay": dict(weight_decay=0.0),
+    "lr_0": dict(lr=0.0, weight_decay=0.5),
+    "heavy_decay": dict(lr=1e-2, weight_decay=50.0),
+    "eps_1": dict(eps=1.0),
+    "clip_inf": dict(max_grad_norm=float("inf")),
+    "zero_grads_clip": dict(max_grad_norm=1.0),
+}
+
+
+@pytest.mark.parametrize("case", list(_DEGENERATE))
+def test_adam_degenerate_hyperparameters(case):
+    """The edge values the update formula admits: either beta 0 (no history,
+    no bias correction), no decay, lr 0 (master unchanged), lr*wd near 1, a
+    large eps, an infinite clip threshold (coefficient 1), and an all-zero
+    gradient under clipping (norm 0: c / 0 is +inf, so coefficient 1)."""
+    kw = dict(max_grad_norm=0.05, inv_loss_scale=2.0 ** -10)
+    kw.update(_DEGENERATE[case])
+    hp = AdamW(**kw)
+    n = 8 * 700 + 5
+    inject = [(i, 0) for i in range(n)] if case == "zero_grads_clip" else None
+    c = _adam_case(n, "bf16", "f16", 2, 5, (1, 1, 1), hp, seed=len(case), inject=inject)
+    st = z.read_grad_stats(c["stats"])
+    s, th, m, v, p = _oracle_step(c, hp, "bf16", "f16", True, st.sq_norm, st.overflow)
+    if case == "zero_grads_clip":
+        assert st.sq_norm == 0.0 and s.coef == 1.0
+    if case == "clip_inf":
+        assert s.coef == 1.0
+    e = check_adam_one_step(hp, s, oracle.value16(c["gb"], "bf16"), c["th0"], c["m0"],
+                            c["v0"], c["th"].host(), c["m"].host(), c["v"].host(), th, m, v,
+                            label=case)
+    check_params16(c["p"].host(), c["th"].host(), th, e["master_scale"], 1e-6, "f16")
+    if case == "lr_0":
+        assert np.array_equal(c["th"].host(), c["th0"] + np.float32(0.0))
+    sa = z.read_adam_state(c["state"])
+    assert sa.step == 1 and sa.skip == 0 and abs(sa.coef - s.coef) <= 1e-12
+    for b in ("g", "th", "m", "v", "p"):
+        assert c[b].canaries_intact(), b
+
+
 @pytest.mark.parametrize("pos", ["head", "middle", "tail"])
 def test_adam_skip_on_overflow(pos):
     hp = AdamW(max_grad_norm=1.0, inv_loss_scale=2.0 ** -16)
