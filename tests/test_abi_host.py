@@ -230,6 +230,11 @@ def test_flatten_stats_validation():
     assert _status(call, ts, numel, "f16", 0, 300, dst, 1.0, dst + 64, need, st_, 0) == z.ZERO_EINVAL
     assert _status(call, ts, numel, "bf16", 250, 60, dst, 1.0, ws, need, st_, 0) == z.ZERO_EINVAL
     assert _status(call, ts, numel, "bf16", 290, 20, dst, 1.0, ws, need, st_, 0) == z.ZERO_EINVAL
+    # workspace inside the second source tensor (which the range reads)
+    ws_in_src = FAKE + (1 << 20) + 64
+    with pytest.raises(z.ZeroError, match="workspace overlaps tensor 1") as e:
+        call(ts, numel, "f16", 0, 300, dst, 1.0, ws_in_src, need, st_, 0)
+    assert e.value.status == z.ZERO_EINVAL
 
 
 def test_flatten_stats_workspace_bound():
@@ -259,4 +264,11 @@ def test_offload_validation_on_host():
     assert _status(call, z.adamw(), g, "f16", h[0] + 2, h[1], h[2], p, "f16", n, None, st, stg, nb,
                    0) == z.ZERO_EALIGN
     assert _status(call, z.adamw(), g, "f16", h[0], h[0] + 4, h[2], p, "f16", n, None, st, stg, nb,
+                   0) == z.ZERO_EINVAL
+    # device buffers: grad / param_out / d_state / d_stats must not overlap
+    assert _status(call, z.adamw(), g, "f16", *h, g + 2 * n - 2, "f16", n, None, st, stg, nb,
+                   0) == z.ZERO_EINVAL
+    assert _status(call, z.adamw(), g, "f16", *h, p, "f16", n, None, p + 8, stg, nb,
+                   0) == z.ZERO_EINVAL
+    assert _status(call, z.adamw(), g, "f16", *h, p, "f16", n, st + 8, st, stg, nb,
                    0) == z.ZERO_EINVAL

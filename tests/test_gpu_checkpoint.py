@@ -144,3 +144,11 @@ def test_ckpt_save_errors(tmp_path):
     with pytest.raises(z.ZeroError) as e:
         z.zero_ckpt_save(str(tmp_path / "x.zck"), n, 2, 2, *bufs, st)
     assert e.value.status == z.ZERO_EINVAL
+    # a save that fails after writing (the target is a directory, so the final
+    # rename fails) leaves neither the target nor its temporary file behind
+    target = tmp_path / "taken"
+    target.mkdir()
+    with pytest.raises(z.ZeroError) as e:
+        z.zero_ckpt_save(str(target), n, 1, 0, *bufs, st)
+    assert e.value.status == z.ZERO_EIO
+    assert target.is_dir() and not (tmp_path / "taken.tmp").exists()

@@ -8,7 +8,9 @@
 // so a crash never leaves a half-written file under the final name.  Load
 // takes the shard files of a saved run with any number of ranks, checks that
 // they describe one run (same psi and step, ranges tiling [0, psi)), and
-// copies the intersection of each file with the loading rank's range.
+// copies the intersection of each file with the loading rank's range.  A save
+// that fails removes its temporary file; a completed one also flushes the
+// directory entry, so the rename itself survives a crash.
 #include <hip/hip_runtime_api.h>
 
 #include <fcntl.h>
@@ -37,6 +39,25 @@ struct Fd {
     int fd = -1;
     ~Fd() { if (fd >= 0) close(fd); }
 };
+
+// Removes the temporary file of a save unless the save completed.
+struct TmpFile {
+    std::string path;
+    bool keep = false;
+    ~TmpFile() { if (!keep) unlink(path.c_str()); }
+};
+
+// Flushes the directory entry of `path` (its parent directory) to storage, so
+// that a completed rename survives a crash.
+bool sync_parent_dir(const char *path)
+{
+    std::string dir(path);
+    const size_t slash = dir.find_last_of('/');
+    dir = slash == std::string::npos ? "." : (slash == 0 ? "/" : dir.substr(0, slash));
+    Fd d;
+    d.fd = open(dir.c_str(), O_RDONLY | O_DIRECTORY);
+    return d.fd >= 0 && fsync(d.fd) == 0;
+}
 
 bool write_all(int fd, const void *buf, size_t len)
 {
@@ -114,6 +135,7 @@ extern "C" zero_status zero_ckpt_save(const char *path, uint64_t psi, uint32_t n
     f.fd = open(tmp.c_str(), O_WRONLY | O_CREAT | O_TRUNC, 0644);
     if (f.fd < 0)
         return fail(ZERO_EIO, "zero_ckpt_save: cannot create %s: %s", tmp.c_str(), strerror(errno));
+    TmpFile guard{tmp};
     if (!write_all(f.fd, &h, sizeof h))
         return fail(ZERO_EIO, "zero_ckpt_save: writing %s: %s", tmp.c_str(), strerror(errno));
     std::vector<char> buf((size_t)std::min<uint64_t>(kChunk, std::max<uint64_t>(4 * n, 1)));
@@ -132,10 +154,16 @@ extern "C" zero_status zero_ckpt_save(const char *path, uint64_t psi, uint32_t n
     }
     if (fsync(f.fd) != 0)
         return fail(ZERO_EIO, "zero_ckpt_save: fsync %s: %s", tmp.c_str(), strerror(errno));
-    close(f.fd);
+    const int fd = f.fd;
     f.fd = -1;
+    if (close(fd) != 0)
+        return fail(ZERO_EIO, "zero_ckpt_save: closing %s: %s", tmp.c_str(), strerror(errno));
     if (rename(tmp.c_str(), path) != 0)
         return fail(ZERO_EIO, "zero_ckpt_save: rename to %s: %s", path, strerror(errno));
+    guard.keep = true;
+    if (!sync_parent_dir(path))
+        return fail(ZERO_EIO, "zero_ckpt_save: syncing the directory of %s: %s", path,
+                    strerror(errno));
     return ZERO_OK;
 }
 

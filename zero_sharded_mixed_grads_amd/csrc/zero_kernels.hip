@@ -746,10 +746,11 @@ uint64_t flatten_tiles_max(const uint64_t *numel, uint32_t n_tensors, uint64_t r
 }
 
 // Shared body of the two gather entry points.  mode: kCopy or a stats mode;
-// part: per-tile partials (stats modes).  *n_tiles: tiles used.
+// part: per-tile partials (stats modes), part_bytes long, which the sources
+// must not overlap either.  *n_tiles: tiles used.
 zero_status flatten_impl(const char *what, const void *const *tensor_ptrs, const uint64_t *numel,
                          uint32_t n_tensors, zero_dtype dt, uint64_t range_begin, uint64_t count,
-                         void *dst, int mode, double *part, hipStream_t stream,
+                         void *dst, int mode, double *part, size_t part_bytes, hipStream_t stream,
                          uint64_t *n_tiles)
 {
     *n_tiles = 0;
@@ -791,6 +792,8 @@ zero_status flatten_impl(const char *what, const void *const *tensor_ptrs, const
                         (unsigned long long)es);
         if (overlap(src + (lo - t_lo) * es, (hi - lo) * es, dst, count * es))
             return fail(ZERO_EINVAL, "%s: dst overlaps tensor %u", what, i);
+        if (overlap(src + (lo - t_lo) * es, (hi - lo) * es, part, part_bytes))
+            return fail(ZERO_EINVAL, "%s: workspace overlaps tensor %u", what, i);
     }
 
     FlatArgs a{};
@@ -883,7 +886,7 @@ extern "C" zero_status zero_bucket_flatten(const void *const *tensor_ptrs, const
         return fail(ZERO_EINVAL, "zero_bucket_flatten: bad dtype %d", (int)dt);
     uint64_t tiles;
     return flatten_impl("zero_bucket_flatten", tensor_ptrs, numel, n_tensors, dt, range_begin,
-                        count, dst, kCopy, nullptr, (hipStream_t)stream, &tiles);
+                        count, dst, kCopy, nullptr, 0, (hipStream_t)stream, &tiles);
 }
 
 extern "C" zero_status zero_grad_stats_workspace(uint64_t n, size_t *bytes)
@@ -991,7 +994,8 @@ extern "C" zero_status zero_bucket_flatten_stats(const void *const *tensor_ptrs,
     uint64_t tiles = 0;
     const zero_status st =
         flatten_impl(what, tensor_ptrs, numel, n_tensors, gdt, range_begin, count, dst,
-                     gdt == ZERO_BF16 ? kStatsBF16 : kStatsF16, (double *)workspace, s, &tiles);
+                     gdt == ZERO_BF16 ? kStatsBF16 : kStatsF16, (double *)workspace, ws_bytes,
+                     s, &tiles);
     if (st != ZERO_OK)
         return st;
     return reduce_partials((double *)workspace, tiles, inv_loss_scale, d_stats, s);

@@ -184,9 +184,14 @@ extern "C" zero_status zero_offload_adam_step(const zero_adamw *hp, const void *
             for (int j = i + 1; j < 4; ++j)
                 if (len[i] && len[j] && host[i] < host[j] + len[j] && host[j] < host[i] + len[i])
                     return fail(ZERO_EINVAL, "%s: host buffers %d and %d overlap", what, i, j);
-        if (n && (uintptr_t)grad < (uintptr_t)param_out + 2 * n &&
-            (uintptr_t)param_out < (uintptr_t)grad + 2 * n)
-            return fail(ZERO_EINVAL, "%s: grad and param_out overlap", what);
+        const uintptr_t dev[4] = {(uintptr_t)grad, (uintptr_t)param_out, (uintptr_t)d_state,
+                                  (uintptr_t)d_stats};
+        const uint64_t dlen[4] = {2 * n, 2 * n, sizeof(zero_adam_state_t),
+                                  d_stats ? sizeof(zero_grad_stats_t) : 0};
+        for (int i = 0; i < 4; ++i)
+            for (int j = i + 1; j < 4; ++j)
+                if (dlen[i] && dlen[j] && dev[i] < dev[j] + dlen[j] && dev[j] < dev[i] + dlen[i])
+                    return fail(ZERO_EINVAL, "%s: device buffers %d and %d overlap", what, i, j);
     }
     hipStream_t s = (hipStream_t)stream;
 
@@ -207,7 +212,13 @@ extern "C" zero_status zero_offload_adam_step(const zero_adamw *hp, const void *
     const RangeFn fn = gb ? (pb ? adamw_range_bb : adamw_range_bh)
                           : (pb ? adamw_range_hb : adamw_range_hh);
 
-    // 2. chunks through two staging slots: slot i holds chunk grads then params
+    // 2. chunks through two staging slots: slot i holds chunk grads then params.
+    // Once a copy is queued, an error still drains the stream before returning,
+    // so no transfer into or out of `staging` outlives the call.
+    auto drain = [s](zero_status r) {
+        (void)hipStreamSynchronize(s);
+        return r;
+    };
     uint16_t *slot_g[2] = {(uint16_t *)staging, (uint16_t *)staging + chunk};
     uint16_t *slot_p[2] = {(uint16_t *)staging + 2 * chunk, (uint16_t *)staging + 3 * chunk};
     Events ev;  // e[0..1]: grads of a slot arrived; e[2..3]: params of a slot sent
@@ -225,22 +236,22 @@ extern "C" zero_status zero_offload_adam_step(const zero_adamw *hp, const void *
         return r != ZERO_OK ? r : hip_ok(hipEventRecord(ev.e[c % 2], s), "event");
     };
     if ((st = fetch(0)) != ZERO_OK)
-        return st;
+        return drain(st);
     for (uint64_t c = 0; c < n_chunks; ++c) {
         if (c + 1 < n_chunks && (st = fetch(c + 1)) != ZERO_OK)
-            return st;
+            return drain(st);
         const int slot = (int)(c % 2);
         if ((st = hip_ok(hipEventSynchronize(ev.e[slot]), "grad copy")) != ZERO_OK)
-            return st;
+            return drain(st);
         if (c >= 2 && (st = hip_ok(hipEventSynchronize(ev.e[2 + slot]), "param copy")) != ZERO_OK)
-            return st;
+            return drain(st);
         const uint64_t lo = c * chunk, cnt = std::min(chunk, n - lo);
         adamw_chunk(fn, k, slot_g[slot], master_host + lo, exp_avg_host + lo,
                     exp_avg_sq_host + lo, slot_p[slot], cnt);
         if ((st = hip_ok(hipMemcpyAsync(pd + lo, slot_p[slot], 2 * cnt, hipMemcpyHostToDevice, s),
                          "param copy")) != ZERO_OK ||
             (st = hip_ok(hipEventRecord(ev.e[2 + slot], s), "event")) != ZERO_OK)
-            return st;
+            return drain(st);
     }
     return hip_ok(hipStreamSynchronize(s), "stream");
 }
