@@ -83,6 +83,9 @@ def lib():
                                 ctypes.c_int, U64]
         L.orc_adamw_f64.argtypes = [ctypes.POINTER(Scalars), VP, ctypes.c_int, VP, VP, VP,
                                     VP, VP, VP, U64]
+        L.orc_loss_scale_init.argtypes = [ctypes.POINTER(Scaler), ctypes.POINTER(ScaleState)]
+        L.orc_loss_scale_update.argtypes = [ctypes.POINTER(Scaler), U32,
+                                            ctypes.POINTER(ScaleState)]
         L.orc_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -189,6 +192,27 @@ def step_scalars(hp, have_stats: bool, sq_norm: float, overflow: int, t_prev: in
     lib().orc_step_scalars(ctypes.byref(h), int(have_stats), sq_norm, overflow, t_prev,
                            ctypes.byref(s))
     return s
+
+
+class Scaler(ctypes.Structure):
+    _fields_ = [("init_scale", DBL), ("growth_factor", DBL), ("backoff_factor", DBL),
+                ("growth_interval", U64), ("min_scale", DBL), ("max_scale", DBL)]
+
+
+class ScaleState(ctypes.Structure):
+    _fields_ = [("scale", DBL), ("inv_scale", DBL), ("good_steps", U64), ("overflows", U64)]
+
+
+def loss_scale_sequence(cfg: Scaler, overflows: Sequence[int]) -> List[Tuple[float, float, int, int]]:
+    """(scale, inv_scale, good_steps, overflows) after each step of a run whose
+    per-step overflow flags are given, starting from cfg.init_scale."""
+    st = ScaleState()
+    lib().orc_loss_scale_init(ctypes.byref(cfg), ctypes.byref(st))
+    out = []
+    for ov in overflows:
+        lib().orc_loss_scale_update(ctypes.byref(cfg), int(bool(ov)), ctypes.byref(st))
+        out.append((st.scale, st.inv_scale, st.good_steps, st.overflows))
+    return out
 
 
 def adamw_(s: Scalars, g_bits: np.ndarray, gdtype: str, master: np.ndarray, m: np.ndarray,

@@ -322,6 +322,60 @@ void orc_adamw_f64(const orc_scalars *s, const uint16_t *g, int g_bf16, const fl
                       &v_out[i]);
 }
 
+/* ------------------------------------------------------------------------
+ * Dynamic loss scaling.  [P2] "メモリ消費の定量化" trains in mixed precision
+ * (fp16 params and grads, fp32 optimizer state) but says nothing about the loss
+ * scale.  The rule taken is dynamic loss scaling as published in Micikevicius
+ * et al., "Mixed Precision Training" (ICLR 2018), section on loss scaling: a
+ * step whose scaled gradients overflow is skipped and the scale is reduced;
+ * after a run of steps without overflow the scale is increased.  With the
+ * usual parameters:
+ *   overflow:  scale <- max(scale * backoff, min_scale); good <- 0
+ *   otherwise: good <- good + 1; when good reaches the growth interval,
+ *              scale <- min(scale * growth, max_scale) if that product is
+ *              finite, and good <- 0.
+ * The parameters are validated by the caller.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    double init_scale, growth_factor, backoff_factor;
+    uint64_t growth_interval;
+    double min_scale, max_scale;
+} orc_scaler;
+
+typedef struct {
+    double scale;
+    double inv_scale;     /* 1 / scale */
+    uint64_t good_steps;  /* steps without overflow since the last change */
+    uint64_t overflows;   /* skipped steps so far */
+} orc_scale_state;
+
+void orc_loss_scale_init(const orc_scaler *c, orc_scale_state *s)
+{
+    s->scale = c->init_scale;
+    s->inv_scale = 1.0 / c->init_scale;
+    s->good_steps = 0;
+    s->overflows = 0;
+}
+
+void orc_loss_scale_update(const orc_scaler *c, uint32_t overflow, orc_scale_state *s)
+{
+    if (overflow) {
+        double reduced = s->scale * c->backoff_factor;
+        s->scale = reduced > c->min_scale ? reduced : c->min_scale;
+        s->good_steps = 0;
+        s->overflows += 1;
+    } else {
+        s->good_steps += 1;
+        if (s->good_steps == c->growth_interval) {
+            double grown = s->scale * c->growth_factor;
+            if (isfinite(grown))
+                s->scale = grown < c->max_scale ? grown : c->max_scale;
+            s->good_steps = 0;
+        }
+    }
+    s->inv_scale = 1.0 / s->scale;
+}
+
 int orc_num_threads(void)
 {
     return omp_get_max_threads();

@@ -44,6 +44,12 @@ MUTANTS = {
     "skip_ignored": ("    if (s->skip)\n        return;\n#pragma omp parallel for",
                      "#pragma omp parallel for"),
     "param_from_old_master": ("        master[i] = (float)pn;\n", ""),
+    "loss_scale_keeps_count_on_overflow": ("        s->good_steps = 0;\n        s->overflows += 1;",
+                                           "        s->overflows += 1;"),
+    "loss_scale_grows_one_step_late": ("if (s->good_steps == c->growth_interval)",
+                                       "if (s->good_steps > c->growth_interval)"),
+    "loss_scale_ignores_floor": ("s->scale = reduced > c->min_scale ? reduced : c->min_scale;",
+                                 "s->scale = reduced;"),
 }
 
 

@@ -543,3 +543,51 @@ def test_adamw_skip_leaves_everything_untouched():
     for a, b in zip((p, m, v), before):
         assert np.array_equal(a, b)
     assert (p16 == 0xABCD).all()
+
+
+# ------------------------------------------------------ dynamic loss scaling
+def _scaler(init=1024.0, growth=2.0, backoff=0.5, interval=3, lo=2.0 ** -100,
+            hi=float("inf")):
+    return oracle.Scaler(init, growth, backoff, interval, lo, hi)
+
+
+@pytest.mark.parametrize("interval", [1, 2, 3, 7])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_loss_scale_matches_torch_amp_update(interval, seed):
+    """Library pin: torch's own loss-scale update (CPU, fp32 scale), which
+    halves the scale on an overflow and doubles it after `interval` steps
+    without one; with power-of-two factors both are exact."""
+    rng = np.random.default_rng(seed)
+    flags = (rng.random(60) < 0.2).astype(int).tolist()
+    got = oracle.loss_scale_sequence(_scaler(interval=interval), flags)
+    scale = torch.tensor([1024.0])
+    tracker = torch.tensor([0], dtype=torch.int32)
+    found = torch.tensor([0.0])
+    for k, ov in enumerate(flags):
+        found.fill_(float(ov))
+        torch._amp_update_scale_(scale, tracker, found, 2.0, 0.5, interval)
+        assert got[k][0] == scale.item(), (k, got[k], scale.item())
+        assert got[k][2] == tracker.item(), (k, got[k], tracker.item())
+        assert got[k][1] == 1.0 / got[k][0]
+    assert got[-1][3] == sum(flags)
+
+
+def test_loss_scale_closed_forms():
+    # k overflows in a row: S0 * b^k, floored at min_scale
+    got = oracle.loss_scale_sequence(_scaler(init=2.0 ** 16, lo=2.0 ** 10), [1] * 9)
+    assert [g[0] for g in got] == [2.0 ** max(16 - k, 10) for k in range(1, 10)]
+    assert [g[3] for g in got] == list(range(1, 10)) and all(g[2] == 0 for g in got)
+    # N good steps: S0 * g^floor(N / I), capped at max_scale; good = N mod I
+    got = oracle.loss_scale_sequence(_scaler(init=8.0, interval=4, hi=2.0 ** 6), [0] * 30)
+    for n, g in enumerate(got, start=1):
+        assert g[0] == min(8.0 * 2.0 ** (n // 4), 2.0 ** 6), (n, g)
+        assert g[2] == n % 4 and g[3] == 0
+    # a non-power-of-two rule, by hand: 1000 -> (x0.25) 250 -> 3 good (x3) 750
+    c = _scaler(init=1000.0, growth=3.0, backoff=0.25, interval=3, lo=1.0)
+    got = oracle.loss_scale_sequence(c, [1, 0, 0, 0, 1, 1, 1, 1, 1])
+    assert [g[0] for g in got] == [250.0, 250.0, 250.0, 750.0, 187.5, 46.875, 11.71875,
+                                   2.9296875, 1.0]
+    # growth that would overflow leaves the scale unchanged but restarts the count
+    big = 2.0 ** 1023
+    got = oracle.loss_scale_sequence(_scaler(init=big, interval=1), [0, 0])
+    assert got == [(big, 1.0 / big, 0, 0)] * 2
