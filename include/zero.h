@@ -137,6 +137,33 @@ typedef struct {
     uint32_t pad;
 } zero_grad_stats_t;
 
+/* Dynamic loss scaling.  [P2] memory accounting trains in mixed fp16/fp32
+ * precision; the pages do not describe the loss scale.  The rule is dynamic
+ * loss scaling as published with mixed-precision training (Micikevicius et
+ * al., "Mixed Precision Training", ICLR 2018): a step whose scaled gradients
+ * overflow is skipped and the scale backs off; after growth_interval steps in
+ * a row without overflow it grows.
+ * Host-side parameters (fp64): */
+typedef struct {
+    double init_scale;       /* starting scale, in [min_scale, max_scale] */
+    double growth_factor;    /* >= 1, finite */
+    double backoff_factor;   /* in (0, 1] */
+    uint64_t growth_interval; /* >= 1 */
+    double min_scale;        /* > 0, finite: floor of the backoff */
+    double max_scale;        /* >= min_scale, may be +inf: cap of the growth */
+} zero_loss_scaler;
+
+/* Device-resident loss-scale state (32 bytes, 8-byte aligned), written by
+ * zero_loss_scale_init and zero_loss_scale_update.  The calls that unscale
+ * gradients accept it in place of a host inv_loss_scale, so that the scale
+ * never has to be read on the host. */
+typedef struct {
+    double scale;        /* the loss scale the next backward multiplies by */
+    double inv_scale;    /* 1 / scale, in fp64 */
+    uint64_t good_steps; /* steps without overflow since the scale last changed */
+    uint64_t overflows;  /* steps skipped so far */
+} zero_loss_scale_t;
+
 /* Bytes of device workspace that zero_grad_stats needs for n gradients. */
 zero_status zero_grad_stats_workspace(uint64_t n, size_t *bytes);
 
@@ -145,19 +172,23 @@ zero_status zero_grad_stats_workspace(uint64_t n, size_t *bytes);
  * ZeRO-DP Stage 2: each rank holds only its part of the gradients).  Reads
  * n 16-bit gradients (gdt F16 or BF16, stored multiplied by the loss
  * scale), and writes *d_stats (device memory) with the overflow flag (any
- * non-finite element) and the squared L2 norm of g * inv_loss_scale,
+ * non-finite element) and the squared L2 norm of g * inv, where inv is
+ * d_scale->inv_scale read on the device when d_scale is not NULL, else the
+ * host value inv_loss_scale (then ignored when d_scale is given); the norm is
  * accumulated in fp64 in a fixed order (bit-reproducible for a given n and
- * 16-byte phase of grad).  sq_norm is unspecified when overflow is set.
+ * 16-byte phase of grad, and equal for the two ways of giving the same inv).
+ * sq_norm is unspecified when overflow is set.
  * n == 0 writes {0, 0}.
  * Multi-rank callers sum sq_norm and take the max of overflow across ranks
  * on the same stream before zero_adam_step.
  * workspace: device memory of at least zero_grad_stats_workspace(n) bytes,
  * 16-byte aligned; its contents are scratch.  Errors: ZERO_EINVAL (NULL
- * grad with n > 0, NULL d_stats, bad dtype, inv_loss_scale not finite and
- * positive), ZERO_ENOSPC (workspace too small), ZERO_EALIGN, ZERO_EDEVICE. */
+ * grad with n > 0, NULL d_stats, bad dtype, no d_scale and inv_loss_scale
+ * not finite and positive, overlapping buffers), ZERO_ENOSPC (workspace too
+ * small), ZERO_EALIGN, ZERO_EDEVICE. */
 zero_status zero_grad_stats(const void *grad, zero_dtype gdt, uint64_t n, double inv_loss_scale,
-                            void *workspace, size_t ws_bytes, zero_grad_stats_t *d_stats,
-                            void *stream);
+                            const zero_loss_scale_t *d_scale, void *workspace, size_t ws_bytes,
+                            zero_grad_stats_t *d_stats, void *stream);
 
 /* Bytes of device workspace that zero_bucket_flatten_stats needs for the
  * elements [range_begin, range_begin + count) of the tensors numel[]. */
@@ -169,7 +200,8 @@ zero_status zero_bucket_flatten_stats_workspace(const uint64_t *numel, uint32_t 
  * [range_begin, range_begin + count) of the list-order flat stream of 16-bit
  * gradient tensors into dst ([P2] ZeRO-R, CB) and, in the same pass, writes
  * *d_stats for the gathered values exactly as zero_grad_stats would for dst
- * (overflow flag; squared L2 norm of g * inv_loss_scale in fp64, summed in a
+ * (overflow flag; squared L2 norm of g * inv in fp64, with inv taken from
+ * d_scale or inv_loss_scale as for zero_grad_stats, summed in a
  * fixed order that depends only on the tensor sizes, the range and dst's
  * 16-byte phase).  Each gradient is read from HBM once instead of twice.  For
  * callers whose gathered range is the rank's final gradient shard: a single
@@ -181,14 +213,15 @@ zero_status zero_bucket_flatten_stats_workspace(const uint64_t *numel, uint32_t 
 zero_status zero_bucket_flatten_stats(const void *const *tensor_ptrs, const uint64_t *numel,
                                       uint32_t n_tensors, zero_dtype gdt, uint64_t range_begin,
                                       uint64_t count, void *dst, double inv_loss_scale,
-                                      void *workspace, size_t ws_bytes, zero_grad_stats_t *d_stats,
-                                      void *stream);
+                                      const zero_loss_scale_t *d_scale, void *workspace,
+                                      size_t ws_bytes, zero_grad_stats_t *d_stats, void *stream);
 
 /* AdamW hyper-parameters (host memory, fp64). */
 typedef struct {
     double lr, beta1, beta2, eps, weight_decay;
     double max_grad_norm;  /* clip by global norm; <= 0 disables clipping */
-    double inv_loss_scale; /* 1 / loss scale applied to the stored gradients */
+    double inv_loss_scale; /* 1 / loss scale applied to the stored gradients
+                            * (ignored when a device loss-scale state is given) */
 } zero_adamw;
 
 /* Device-resident step state (64 bytes, 8-byte aligned).  The caller
@@ -212,27 +245,50 @@ typedef struct {
  * accounting fixes the arrays: 16-bit params and grads, fp32 master,
  * momentum and variance; [P4] 显存背景 names the optimizer AdamW.
  * For every element i < n of the shard:
- *   g  = grad[i] * inv_loss_scale * coef
+ *   g  = grad[i] * inv * coef
  *   m  = beta1 m + (1 - beta1) g;   v = beta2 v + (1 - beta2) g^2
  *   master = master - lr wd master - lr (m / (1 - beta1^t)) /
  *            (sqrt(v / (1 - beta2^t)) + eps)
  *   param_out[i] = master rounded to pdt (nearest, ties to even)
- * with t the advanced step count and coef = min(1, max_grad_norm / ||g||)
+ * with t the advanced step count, coef = min(1, max_grad_norm / ||g||)
  * (1 when clipping is off or d_stats is NULL), computed in fp64 on the
- * device from *d_stats.  If d_stats reports overflow, the step is skipped:
+ * device from *d_stats, and inv = d_scale->inv_scale (read on the device)
+ * when d_scale is not NULL, else hp->inv_loss_scale.  With dynamic loss
+ * scaling, call zero_loss_scale_update after this call, on the same stream,
+ * so that the step uses the scale its gradients were computed with.  If d_stats reports overflow, the step is skipped:
  * nothing is written to the arrays and `step` does not advance.
  * grad: n 16-bit gradients (gdt); master, exp_avg, exp_avg_sq: n fp32 each,
  * updated in place; param_out: n 16-bit params (pdt), written.  d_stats:
  * device result of zero_grad_stats (or NULL: no clipping, never skip);
  * d_state: device step state.  n == 0 still advances d_state.
  * Errors: ZERO_EINVAL (NULL hp or d_state, NULL arrays with n > 0, bad
- * dtypes, lr < 0, beta outside [0, 1), eps <= 0, weight_decay < 0,
- * inv_loss_scale not finite and positive, NaN max_grad_norm, overlapping
- * arrays), ZERO_EALIGN, ZERO_EDEVICE. */
+ * dtypes, lr < 0, beta outside [0, 1), eps <= 0, weight_decay < 0, no
+ * d_scale and inv_loss_scale not finite and positive, NaN max_grad_norm,
+ * overlapping arrays), ZERO_EALIGN, ZERO_EDEVICE. */
 zero_status zero_adam_step(const zero_adamw *hp, const void *grad, zero_dtype gdt, float *master,
                            float *exp_avg, float *exp_avg_sq, void *param_out, zero_dtype pdt,
                            uint64_t n, const zero_grad_stats_t *d_stats,
-                           zero_adam_state_t *d_state, void *stream);
+                           const zero_loss_scale_t *d_scale, zero_adam_state_t *d_state,
+                           void *stream);
+
+/* Sets *d_scale (device) to {cfg->init_scale, 1 / init_scale, 0, 0} with a
+ * one-thread kernel, ordered on `stream`.  Errors: ZERO_EINVAL (NULL
+ * arguments, parameters outside the domains above), ZERO_EALIGN,
+ * ZERO_EDEVICE. */
+zero_status zero_loss_scale_init(const zero_loss_scaler *cfg, zero_loss_scale_t *d_scale,
+                                 void *stream);
+
+/* Advances *d_scale after a step from that step's *d_stats, on the device:
+ *   overflow:  scale = max(scale * backoff_factor, min_scale), good_steps = 0,
+ *              overflows += 1 (the step itself was skipped);
+ *   otherwise: good_steps += 1; when it reaches growth_interval,
+ *              scale = min(scale * growth_factor, max_scale) if that product
+ *              is finite, and good_steps = 0;
+ * then inv_scale = 1 / scale (fp64).  Errors: ZERO_EINVAL (NULL arguments,
+ * parameters outside their domains, overlapping d_stats and d_scale),
+ * ZERO_EALIGN, ZERO_EDEVICE. */
+zero_status zero_loss_scale_update(const zero_loss_scaler *cfg, const zero_grad_stats_t *d_stats,
+                                   zero_loss_scale_t *d_scale, void *stream);
 
 /* --------------------------------------------- optimizer state in host memory */
 
@@ -248,8 +304,9 @@ zero_status zero_offload_staging_bytes(uint64_t chunk_elems, size_t *bytes);
  * zero_adam_step, with the fp32 master, exp_avg and exp_avg_sq in HOST memory
  * (n elements each, updated in place by host threads) while the 16-bit grad
  * and param_out stay on the device.  The step state d_state and the optional
- * statistics d_stats are device-resident, as for zero_adam_step, and the
- * skip, clip and bias corrections are computed the same way.  The gradients
+ * statistics d_stats and loss-scale state d_scale are device-resident, as
+ * for zero_adam_step, and the skip, clip and bias corrections are computed
+ * the same way.  The gradients
  * travel device -> host and the new 16-bit params host -> device in chunks
  * of staging_bytes / 8 elements through `staging`, caller-owned pinned host
  * memory (e.g. from hipHostMalloc), two slots deep so that transfers overlap
@@ -262,8 +319,8 @@ zero_status zero_offload_adam_step(const zero_adamw *hp, const void *grad, zero_
                                    float *master_host, float *exp_avg_host,
                                    float *exp_avg_sq_host, void *param_out, zero_dtype pdt,
                                    uint64_t n, const zero_grad_stats_t *d_stats,
-                                   zero_adam_state_t *d_state, void *staging,
-                                   size_t staging_bytes, void *stream);
+                                   const zero_loss_scale_t *d_scale, zero_adam_state_t *d_state,
+                                   void *staging, size_t staging_bytes, void *stream);
 
 /* ------------------------------------------------------ sharded checkpoints */
 

@@ -23,7 +23,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     assert set(names) == set(z.EXPORTS)
     L = ctypes.CDLL(z.LIB_PATH)
     for name in names:
@@ -272,3 +272,41 @@ def test_offload_validation_on_host():
                    0) == z.ZERO_EINVAL
     assert _status(call, z.adamw(), g, "f16", *h, p, "f16", n, st + 8, st, stg, nb,
                    0) == z.ZERO_EINVAL
+
+
+def test_loss_scale_validation_on_host():
+    """Parameter domains, alignment and overlap are rejected before any
+    device access; with a device loss-scale state the host inv_loss_scale is
+    not checked."""
+    d, st_ = FAKE + (20 << 20), FAKE + (21 << 20)
+    ok = z.loss_scaler()
+    bad = [z.loss_scaler(min_scale=0.0), z.loss_scaler(min_scale=float("nan")),
+           z.loss_scaler(max_scale=0.5), z.loss_scaler(init_scale=0.5),
+           z.loss_scaler(init_scale=float("inf"), max_scale=float("inf")),
+           z.loss_scaler(growth_factor=0.5), z.loss_scaler(growth_factor=float("inf")),
+           z.loss_scaler(backoff_factor=0.0), z.loss_scaler(backoff_factor=1.5),
+           z.loss_scaler(growth_interval=0)]
+    for cfg in bad:
+        assert _status(z.zero_loss_scale_init, cfg, d, 0) == z.ZERO_EINVAL
+        assert _status(z.zero_loss_scale_update, cfg, st_, d, 0) == z.ZERO_EINVAL
+    assert _status(z.zero_loss_scale_init, ok, None, 0) == z.ZERO_EINVAL
+    assert _status(z.zero_loss_scale_init, ok, d + 4, 0) == z.ZERO_EALIGN
+    assert _status(z.zero_loss_scale_update, ok, None, d, 0) == z.ZERO_EINVAL
+    assert _status(z.zero_loss_scale_update, ok, st_, d + 4, 0) == z.ZERO_EALIGN
+    assert _status(z.zero_loss_scale_update, ok, d + 16, d, 0) == z.ZERO_EINVAL  # overlap
+    # consumers: misaligned or overlapping d_scale
+    n = 1 << 12
+    g, ws = FAKE, FAKE + (1 << 20)
+    wsb = z.zero_grad_stats_workspace(n)
+    assert _status(z.zero_grad_stats, g, "f16", n, 1.0, ws, wsb, st_, 0, d + 4) == z.ZERO_EALIGN
+    assert _status(z.zero_grad_stats, g, "f16", n, 1.0, ws, wsb, st_, 0, st_) == z.ZERO_EINVAL
+    # without a device state a bad host inv_loss_scale is rejected
+    assert _status(z.zero_grad_stats, g, "f16", n, 0.0, ws, wsb, st_, 0) == z.ZERO_EINVAL
+    h = [FAKE + ((30 + i) << 20) for i in range(5)]
+    stt = FAKE + (40 << 20)
+    assert _status(z.zero_adam_step, z.adamw(inv_loss_scale=0.0), h[0], "f16", h[1], h[2], h[3],
+                   h[4], "f16", n, None, stt, 0) == z.ZERO_EINVAL
+    assert _status(z.zero_adam_step, z.adamw(), h[0], "f16", h[1], h[2], h[3], h[4], "f16", n,
+                   None, stt, 0, h[1] + 64) == z.ZERO_EINVAL  # d_scale inside master
+    assert _status(z.zero_adam_step, z.adamw(), h[0], "f16", h[1], h[2], h[3], h[4], "f16", n,
+                   None, stt, 0, d + 4) == z.ZERO_EALIGN

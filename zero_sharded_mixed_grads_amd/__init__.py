@@ -55,6 +55,15 @@ class AdamState(ctypes.Structure):  # zero_adam_state_t, device resident
                 ("decay", ctypes.c_float), ("pad1", U32)]
 
 
+class LossScaler(ctypes.Structure):  # zero_loss_scaler, host parameters
+    _fields_ = [("init_scale", DBL), ("growth_factor", DBL), ("backoff_factor", DBL),
+                ("growth_interval", U64), ("min_scale", DBL), ("max_scale", DBL)]
+
+
+class LossScale(ctypes.Structure):  # zero_loss_scale_t, device resident
+    _fields_ = [("scale", DBL), ("inv_scale", DBL), ("good_steps", U64), ("overflows", U64)]
+
+
 class CkptHeader(ctypes.Structure):  # zero_ckpt_header
     _fields_ = [("magic", ctypes.c_char * 8), ("version", U32), ("nd", U32), ("rank", U32),
                 ("pad", U32), ("psi", U64), ("begin", U64), ("end", U64), ("step", U64),
@@ -63,12 +72,14 @@ class CkptHeader(ctypes.Structure):  # zero_ckpt_header
 
 assert ctypes.sizeof(GradStats) == 16 and ctypes.sizeof(AdamState) == 64
 assert ctypes.sizeof(CkptHeader) == 64
+assert ctypes.sizeof(LossScaler) == 48 and ctypes.sizeof(LossScale) == 32
 
 EXPORTS = ("zero_status_str", "zero_last_error", "zero_partition", "zero_mem_bytes",
            "zero_bucket_plan", "zero_bucket_flatten", "zero_grad_stats_workspace",
            "zero_grad_stats", "zero_bucket_flatten_stats_workspace", "zero_bucket_flatten_stats",
            "zero_adam_step", "zero_offload_staging_bytes", "zero_offload_adam_step",
-           "zero_ckpt_save", "zero_ckpt_read_header", "zero_ckpt_load")
+           "zero_ckpt_save", "zero_ckpt_read_header", "zero_ckpt_load",
+           "zero_loss_scale_init", "zero_loss_scale_update")
 
 _lib = None
 
@@ -92,17 +103,20 @@ def lib():
         L.zero_bucket_flatten.argtypes = [ctypes.POINTER(VP), ctypes.POINTER(U64), U32,
                                           ctypes.c_int, U64, U64, VP, VP]
         L.zero_grad_stats_workspace.argtypes = [U64, ctypes.POINTER(ctypes.c_size_t)]
-        L.zero_grad_stats.argtypes = [VP, ctypes.c_int, U64, DBL, VP, ctypes.c_size_t, VP, VP]
+        L.zero_grad_stats.argtypes = [VP, ctypes.c_int, U64, DBL, VP, VP, ctypes.c_size_t, VP,
+                                      VP]
         L.zero_bucket_flatten_stats_workspace.argtypes = [ctypes.POINTER(U64), U32, U64, U64,
                                                           ctypes.POINTER(ctypes.c_size_t)]
         L.zero_bucket_flatten_stats.argtypes = [ctypes.POINTER(VP), ctypes.POINTER(U64), U32,
-                                                ctypes.c_int, U64, U64, VP, DBL, VP,
+                                                ctypes.c_int, U64, U64, VP, DBL, VP, VP,
                                                 ctypes.c_size_t, VP, VP]
         L.zero_adam_step.argtypes = [ctypes.POINTER(AdamW), VP, ctypes.c_int, VP, VP, VP, VP,
-                                     ctypes.c_int, U64, VP, VP, VP]
+                                     ctypes.c_int, U64, VP, VP, VP, VP]
+        L.zero_loss_scale_init.argtypes = [ctypes.POINTER(LossScaler), VP, VP]
+        L.zero_loss_scale_update.argtypes = [ctypes.POINTER(LossScaler), VP, VP, VP]
         L.zero_offload_staging_bytes.argtypes = [U64, ctypes.POINTER(ctypes.c_size_t)]
         L.zero_offload_adam_step.argtypes = [ctypes.POINTER(AdamW), VP, ctypes.c_int, VP, VP,
-                                             VP, VP, ctypes.c_int, U64, VP, VP, VP,
+                                             VP, VP, ctypes.c_int, U64, VP, VP, VP, VP,
                                              ctypes.c_size_t, VP]
         L.zero_ckpt_save.argtypes = [ctypes.c_char_p, U64, U32, U32, VP, VP, VP, VP, VP]
         L.zero_ckpt_read_header.argtypes = [ctypes.c_char_p, ctypes.POINTER(CkptHeader)]
@@ -193,9 +207,11 @@ def zero_grad_stats_workspace(n: int) -> int:
 
 
 def zero_grad_stats(grad, gdtype, n: int, inv_loss_scale: float, workspace, ws_bytes: int,
-                    d_stats, stream=None) -> None:
-    _check(lib().zero_grad_stats(_ptr(grad), _dtype(gdtype), n, inv_loss_scale, _ptr(workspace),
-                                 ws_bytes, _ptr(d_stats), _stream(stream)))
+                    d_stats, stream=None, d_scale=None) -> None:
+    """d_scale: optional device zero_loss_scale_t whose inv_scale replaces
+    inv_loss_scale (read on the device)."""
+    _check(lib().zero_grad_stats(_ptr(grad), _dtype(gdtype), n, inv_loss_scale, _ptr(d_scale),
+                                 _ptr(workspace), ws_bytes, _ptr(d_stats), _stream(stream)))
 
 
 def zero_bucket_flatten_stats_workspace(numel: Sequence[int], range_begin: int,
@@ -209,21 +225,33 @@ def zero_bucket_flatten_stats_workspace(numel: Sequence[int], range_begin: int,
 
 def zero_bucket_flatten_stats(tensors: Sequence, numel: Optional[Sequence[int]], gdtype,
                               range_begin: int, count: int, dst, inv_loss_scale: float,
-                              workspace, ws_bytes: int, d_stats, stream=None) -> None:
+                              workspace, ws_bytes: int, d_stats, stream=None,
+                              d_scale=None) -> None:
     if numel is None:
         numel = [t.numel() for t in tensors]
     ptrs = (VP * len(tensors))(*[_ptr(t) for t in tensors])
     nums = (U64 * len(numel))(*numel)
     _check(lib().zero_bucket_flatten_stats(ptrs, nums, len(tensors), _dtype(gdtype), range_begin,
-                                           count, _ptr(dst), inv_loss_scale, _ptr(workspace),
-                                           ws_bytes, _ptr(d_stats), _stream(stream)))
+                                           count, _ptr(dst), inv_loss_scale, _ptr(d_scale),
+                                           _ptr(workspace), ws_bytes, _ptr(d_stats),
+                                           _stream(stream)))
 
 
 def zero_adam_step(hp: AdamW, grad, gdtype, master, exp_avg, exp_avg_sq, param_out, pdtype,
-                   n: int, d_stats, d_state, stream=None) -> None:
+                   n: int, d_stats, d_state, stream=None, d_scale=None) -> None:
     _check(lib().zero_adam_step(ctypes.byref(hp), _ptr(grad), _dtype(gdtype), _ptr(master),
                                 _ptr(exp_avg), _ptr(exp_avg_sq), _ptr(param_out), _dtype(pdtype),
-                                n, _ptr(d_stats), _ptr(d_state), _stream(stream)))
+                                n, _ptr(d_stats), _ptr(d_scale), _ptr(d_state),
+                                _stream(stream)))
+
+
+def zero_loss_scale_init(cfg: LossScaler, d_scale, stream=None) -> None:
+    _check(lib().zero_loss_scale_init(ctypes.byref(cfg), _ptr(d_scale), _stream(stream)))
+
+
+def zero_loss_scale_update(cfg: LossScaler, d_stats, d_scale, stream=None) -> None:
+    _check(lib().zero_loss_scale_update(ctypes.byref(cfg), _ptr(d_stats), _ptr(d_scale),
+                                        _stream(stream)))
 
 
 # ------------------------------------------ optimizer state in host memory
@@ -235,14 +263,14 @@ def zero_offload_staging_bytes(chunk_elems: int) -> int:
 
 def zero_offload_adam_step(hp: AdamW, grad, gdtype, master_host, exp_avg_host, exp_avg_sq_host,
                            param_out, pdtype, n: int, d_stats, d_state, staging,
-                           staging_bytes: int, stream=None) -> None:
+                           staging_bytes: int, stream=None, d_scale=None) -> None:
     """master/exp_avg/exp_avg_sq: host tensors (or addresses); staging: pinned
     host memory; grad, param_out, d_stats, d_state: device."""
     _check(lib().zero_offload_adam_step(ctypes.byref(hp), _ptr(grad), _dtype(gdtype),
                                         _ptr(master_host), _ptr(exp_avg_host),
                                         _ptr(exp_avg_sq_host), _ptr(param_out), _dtype(pdtype),
-                                        n, _ptr(d_stats), _ptr(d_state), _ptr(staging),
-                                        staging_bytes, _stream(stream)))
+                                        n, _ptr(d_stats), _ptr(d_scale), _ptr(d_state),
+                                        _ptr(staging), staging_bytes, _stream(stream)))
 
 
 # ---------------------------------------------------- sharded checkpoints
@@ -274,6 +302,22 @@ def new_grad_stats(device) -> torch.Tensor:
 def new_adam_state(device) -> torch.Tensor:
     """A zeroed device buffer for one zero_adam_state_t (step 0)."""
     return torch.zeros(ctypes.sizeof(AdamState), dtype=torch.uint8, device=device)
+
+
+def new_loss_scale(device) -> torch.Tensor:
+    """A device buffer for one zero_loss_scale_t (set it with zero_loss_scale_init)."""
+    return torch.zeros(ctypes.sizeof(LossScale), dtype=torch.uint8, device=device)
+
+
+def read_loss_scale(buf: torch.Tensor) -> LossScale:
+    """Synchronising copy of a device zero_loss_scale_t."""
+    return LossScale.from_buffer_copy(bytes(buf.cpu().numpy()))
+
+
+def loss_scaler(init_scale=2.0 ** 16, growth_factor=2.0, backoff_factor=0.5,
+                growth_interval=2000, min_scale=1.0, max_scale=float("inf")) -> LossScaler:
+    return LossScaler(init_scale, growth_factor, backoff_factor, growth_interval, min_scale,
+                      max_scale)
 
 
 def new_workspace(n: int, device) -> torch.Tensor:

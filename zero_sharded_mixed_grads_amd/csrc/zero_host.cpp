@@ -28,7 +28,7 @@ zero_status fail(zero_status s, const char *fmt, ...)
     return s;
 }
 
-zero_status check_adamw(const zero_adamw &hp, const char *what)
+zero_status check_adamw(const zero_adamw &hp, bool host_inv_scale, const char *what)
 {
     if (!(hp.lr >= 0.0 && std::isfinite(hp.lr)))
         return fail(ZERO_EINVAL, "%s: lr must be finite and >= 0", what);
@@ -38,10 +38,29 @@ zero_status check_adamw(const zero_adamw &hp, const char *what)
         return fail(ZERO_EINVAL, "%s: eps must be finite and > 0", what);
     if (!(hp.weight_decay >= 0.0 && std::isfinite(hp.weight_decay)))
         return fail(ZERO_EINVAL, "%s: weight_decay must be finite and >= 0", what);
-    if (!(std::isfinite(hp.inv_loss_scale) && hp.inv_loss_scale > 0.0))
+    if (host_inv_scale && !(std::isfinite(hp.inv_loss_scale) && hp.inv_loss_scale > 0.0))
         return fail(ZERO_EINVAL, "%s: inv_loss_scale must be finite and > 0", what);
     if (std::isnan(hp.max_grad_norm))
         return fail(ZERO_EINVAL, "%s: max_grad_norm is NaN", what);
+    return ZERO_OK;
+}
+
+zero_status check_scaler(const zero_loss_scaler &c, const char *what)
+{
+    if (!(c.min_scale > 0.0 && std::isfinite(c.min_scale)))
+        return fail(ZERO_EINVAL, "%s: min_scale must be finite and > 0", what);
+    if (!(c.max_scale >= c.min_scale))  // +inf allowed, NaN rejected
+        return fail(ZERO_EINVAL, "%s: max_scale must be >= min_scale", what);
+    if (!(c.init_scale >= c.min_scale && c.init_scale <= c.max_scale &&
+          std::isfinite(c.init_scale)))
+        return fail(ZERO_EINVAL, "%s: init_scale must be finite and in [min_scale, max_scale]",
+                    what);
+    if (!(c.growth_factor >= 1.0 && std::isfinite(c.growth_factor)))
+        return fail(ZERO_EINVAL, "%s: growth_factor must be finite and >= 1", what);
+    if (!(c.backoff_factor > 0.0 && c.backoff_factor <= 1.0))
+        return fail(ZERO_EINVAL, "%s: backoff_factor must be in (0, 1]", what);
+    if (c.growth_interval == 0)
+        return fail(ZERO_EINVAL, "%s: growth_interval must be >= 1", what);
     return ZERO_OK;
 }
 

@@ -481,8 +481,13 @@ __global__ void __launch_bounds__(kBlock)
 }
 
 __global__ void __launch_bounds__(kBlock)
-    stats_final(const double *in, uint64_t n_in, double inv_scale_sq, zero_grad_stats_t *out)
+    stats_final(const double *in, uint64_t n_in, double inv_scale_sq,
+                const zero_loss_scale_t *scale, zero_grad_stats_t *out)
 {
+    if (scale) {  // the device loss-scale state replaces the host value
+        const double inv = scale->inv_scale;
+        inv_scale_sq = inv * inv;
+    }
     double s = 0.0;
     for (uint64_t k = threadIdx.x; k < n_in; k += kBlock)
         s += in[k];
@@ -498,7 +503,7 @@ __global__ void __launch_bounds__(kBlock)
 // ================================================================= AdamW
 // Per-step scalars, computed once in fp64 by one thread and rounded once.
 __global__ void adam_scalars(zero_adamw hp, const zero_grad_stats_t *stats,
-                             zero_adam_state_t *st)
+                             const zero_loss_scale_t *scale, zero_adam_state_t *st)
 {
     if (threadIdx.x != 0 || blockIdx.x != 0)
         return;
@@ -522,7 +527,8 @@ __global__ void adam_scalars(zero_adamw hp, const zero_grad_stats_t *stats,
     st->step = t;
     st->skip = 0;
     st->coef = coef;
-    st->grad_mult = (float)(hp.inv_loss_scale * coef);
+    const double inv = scale ? scale->inv_scale : hp.inv_loss_scale;
+    st->grad_mult = (float)(inv * coef);
     st->step_size = (float)(hp.lr / bc1);
     st->inv_sqrt_bc2 = (float)(1.0 / sqrt(bc2));
     st->beta1 = (float)hp.beta1;
@@ -531,6 +537,42 @@ __global__ void adam_scalars(zero_adamw hp, const zero_grad_stats_t *stats,
     st->one_minus_beta2 = (float)(1.0 - hp.beta2);
     st->eps = (float)hp.eps;
     st->decay = (float)(hp.lr * hp.weight_decay);
+}
+
+// Dynamic loss scaling (Micikevicius et al., "Mixed Precision Training"): one
+// thread sets or advances the device-resident scale state.
+__global__ void loss_scale_init(zero_loss_scaler c, zero_loss_scale_t *d)
+{
+    if (threadIdx.x != 0 || blockIdx.x != 0)
+        return;
+    d->scale = c.init_scale;
+    d->inv_scale = 1.0 / c.init_scale;
+    d->good_steps = 0;
+    d->overflows = 0;
+}
+
+__global__ void loss_scale_update(zero_loss_scaler c, const zero_grad_stats_t *stats,
+                                  zero_loss_scale_t *d)
+{
+    if (threadIdx.x != 0 || blockIdx.x != 0)
+        return;
+    double scale = d->scale;
+    uint64_t good = d->good_steps, overflows = d->overflows;
+    if (stats->overflow) {  // the step was skipped: back off
+        const double reduced = scale * c.backoff_factor;
+        scale = reduced > c.min_scale ? reduced : c.min_scale;
+        good = 0;
+        ++overflows;
+    } else if (++good == c.growth_interval) {  // a full run without overflow: grow
+        const double grown = scale * c.growth_factor;
+        if (__builtin_isfinite(grown))
+            scale = grown < c.max_scale ? grown : c.max_scale;
+        good = 0;
+    }
+    d->scale = scale;
+    d->inv_scale = 1.0 / scale;
+    d->good_steps = good;
+    d->overflows = overflows;
 }
 
 struct AdamArgs {
@@ -847,8 +889,8 @@ zero_status flatten_impl(const char *what, const void *const *tensor_ptrs, const
 namespace {
 // Fixed-order reduction of `tiles` per-tile partials (at part) into *out:
 // groups of kReduceGroup when there are many, then one block.
-zero_status reduce_partials(double *part, uint64_t tiles, double inv_scale, zero_grad_stats_t *out,
-                            hipStream_t s)
+zero_status reduce_partials(double *part, uint64_t tiles, double inv_scale,
+                            const zero_loss_scale_t *scale, zero_grad_stats_t *out, hipStream_t s)
 {
     const double *last = part;
     uint64_t n_last = tiles;
@@ -864,16 +906,17 @@ zero_status reduce_partials(double *part, uint64_t tiles, double inv_scale, zero
         n_last = groups;
     }
     hipLaunchKernelGGL(stats_final, dim3(1), dim3(kBlock), 0, s, last, n_last,
-                       inv_scale * inv_scale, out);
+                       inv_scale * inv_scale, scale, out);
     return launch_status("gradient statistics: final");
 }
 }  // namespace
 
 zero_status zero::launch_adam_scalars(const zero_adamw &hp, const zero_grad_stats_t *d_stats,
+                                      const zero_loss_scale_t *d_scale,
                                       zero_adam_state_t *d_state, void *stream)
 {
     hipLaunchKernelGGL(adam_scalars, dim3(1), dim3(64), 0, (hipStream_t)stream, hp, d_stats,
-                       d_state);
+                       d_scale, d_state);
     return launch_status("adam step scalars");
 }
 
@@ -898,15 +941,18 @@ extern "C" zero_status zero_grad_stats_workspace(uint64_t n, size_t *bytes)
 }
 
 extern "C" zero_status zero_grad_stats(const void *grad, zero_dtype gdt, uint64_t n,
-                                       double inv_loss_scale, void *workspace, size_t ws_bytes,
+                                       double inv_loss_scale, const zero_loss_scale_t *d_scale,
+                                       void *workspace, size_t ws_bytes,
                                        zero_grad_stats_t *d_stats, void *stream)
 {
     if (gdt != ZERO_F16 && gdt != ZERO_BF16)
         return fail(ZERO_EINVAL, "zero_grad_stats: gradient dtype must be F16 or BF16");
     if (!d_stats)
         return fail(ZERO_EINVAL, "zero_grad_stats: NULL d_stats");
-    if (!(std::isfinite(inv_loss_scale) && inv_loss_scale > 0.0))
+    if (!d_scale && !(std::isfinite(inv_loss_scale) && inv_loss_scale > 0.0))
         return fail(ZERO_EINVAL, "zero_grad_stats: inv_loss_scale must be finite and > 0");
+    if (d_scale)
+        inv_loss_scale = 1.0;  // unused: the kernel reads the device state
     if (n > 0 && !grad)
         return fail(ZERO_EINVAL, "zero_grad_stats: NULL grad");
     if (n > UINT64_MAX / 4)
@@ -916,10 +962,13 @@ extern "C" zero_status zero_grad_stats(const void *grad, zero_dtype gdt, uint64_
     const size_t need = stats_workspace_bytes(n);
     if (ws_bytes < need)
         return fail(ZERO_ENOSPC, "zero_grad_stats: workspace %zu bytes < %zu", ws_bytes, need);
-    if (!aligned(grad, 2) || !aligned(workspace, 16) || !aligned(d_stats, 8))
+    if (!aligned(grad, 2) || !aligned(workspace, 16) || !aligned(d_stats, 8) ||
+        !aligned(d_scale, 8))
         return fail(ZERO_EALIGN, "zero_grad_stats: misaligned pointer");
     if (overlap(workspace, ws_bytes, d_stats, sizeof *d_stats) ||
-        overlap(workspace, ws_bytes, grad, 2 * n) || overlap(d_stats, sizeof *d_stats, grad, 2 * n))
+        overlap(workspace, ws_bytes, grad, 2 * n) || overlap(d_stats, sizeof *d_stats, grad, 2 * n) ||
+        (d_scale && (overlap(d_scale, sizeof *d_scale, workspace, ws_bytes) ||
+                     overlap(d_scale, sizeof *d_scale, d_stats, sizeof *d_stats))))
         return fail(ZERO_EINVAL, "zero_grad_stats: overlapping buffers");
     hipStream_t s = (hipStream_t)stream;
     const uint64_t ph = ((uintptr_t)grad & 15u) / 2;
@@ -942,7 +991,7 @@ extern "C" zero_status zero_grad_stats(const void *grad, zero_dtype gdt, uint64_
     const zero_status st = launch_status("zero_grad_stats pass 1");
     if (st != ZERO_OK)
         return st;
-    return reduce_partials(part, tiles, inv_loss_scale, d_stats, s);
+    return reduce_partials(part, tiles, inv_loss_scale, d_scale, d_stats, s);
 }
 
 extern "C" zero_status zero_bucket_flatten_stats_workspace(const uint64_t *numel, uint32_t n_tensors,
@@ -964,6 +1013,7 @@ extern "C" zero_status zero_bucket_flatten_stats(const void *const *tensor_ptrs,
                                                  const uint64_t *numel, uint32_t n_tensors,
                                                  zero_dtype gdt, uint64_t range_begin,
                                                  uint64_t count, void *dst, double inv_loss_scale,
+                                                 const zero_loss_scale_t *d_scale,
                                                  void *workspace, size_t ws_bytes,
                                                  zero_grad_stats_t *d_stats, void *stream)
 {
@@ -972,8 +1022,10 @@ extern "C" zero_status zero_bucket_flatten_stats(const void *const *tensor_ptrs,
         return fail(ZERO_EINVAL, "%s: gradient dtype must be F16 or BF16", what);
     if (!d_stats)
         return fail(ZERO_EINVAL, "%s: NULL d_stats", what);
-    if (!(std::isfinite(inv_loss_scale) && inv_loss_scale > 0.0))
+    if (!d_scale && !(std::isfinite(inv_loss_scale) && inv_loss_scale > 0.0))
         return fail(ZERO_EINVAL, "%s: inv_loss_scale must be finite and > 0", what);
+    if (d_scale)
+        inv_loss_scale = 1.0;  // unused: the kernel reads the device state
     if (!workspace)
         return fail(ZERO_EINVAL, "%s: NULL workspace", what);
     if (n_tensors > 0 && !numel)
@@ -984,11 +1036,14 @@ extern "C" zero_status zero_bucket_flatten_stats(const void *const *tensor_ptrs,
     const size_t need = partials_bytes(flatten_tiles_max(numel, n_tensors, range_begin, range_end));
     if (ws_bytes < need)
         return fail(ZERO_ENOSPC, "%s: workspace %zu bytes < %zu", what, ws_bytes, need);
-    if (!aligned(workspace, 16) || !aligned(d_stats, 8))
-        return fail(ZERO_EALIGN, "%s: misaligned workspace or d_stats", what);
+    if (!aligned(workspace, 16) || !aligned(d_stats, 8) || !aligned(d_scale, 8))
+        return fail(ZERO_EALIGN, "%s: misaligned workspace, d_stats or d_scale", what);
     if (overlap(workspace, ws_bytes, d_stats, sizeof *d_stats) ||
         overlap(workspace, ws_bytes, dst, 2 * count) ||
-        overlap(d_stats, sizeof *d_stats, dst, 2 * count))
+        overlap(d_stats, sizeof *d_stats, dst, 2 * count) ||
+        (d_scale && (overlap(d_scale, sizeof *d_scale, workspace, ws_bytes) ||
+                     overlap(d_scale, sizeof *d_scale, d_stats, sizeof *d_stats) ||
+                     overlap(d_scale, sizeof *d_scale, dst, 2 * count))))
         return fail(ZERO_EINVAL, "%s: overlapping buffers", what);
     hipStream_t s = (hipStream_t)stream;
     uint64_t tiles = 0;
@@ -998,7 +1053,7 @@ extern "C" zero_status zero_bucket_flatten_stats(const void *const *tensor_ptrs,
                      s, &tiles);
     if (st != ZERO_OK)
         return st;
-    return reduce_partials((double *)workspace, tiles, inv_loss_scale, d_stats, s);
+    return reduce_partials((double *)workspace, tiles, inv_loss_scale, d_scale, d_stats, s);
 }
 
 namespace {
@@ -1035,7 +1090,8 @@ void launch_adam(const AdamArgs &a, uint64_t work, hipStream_t s)
 extern "C" zero_status zero_adam_step(const zero_adamw *hp, const void *grad, zero_dtype gdt,
                                       float *master, float *exp_avg, float *exp_avg_sq,
                                       void *param_out, zero_dtype pdt, uint64_t n,
-                                      const zero_grad_stats_t *d_stats, zero_adam_state_t *d_state,
+                                      const zero_grad_stats_t *d_stats,
+                                      const zero_loss_scale_t *d_scale, zero_adam_state_t *d_state,
                                       void *stream)
 {
     if (!hp)
@@ -1044,7 +1100,8 @@ extern "C" zero_status zero_adam_step(const zero_adamw *hp, const void *grad, ze
         return fail(ZERO_EINVAL, "zero_adam_step: NULL d_state");
     if ((gdt != ZERO_F16 && gdt != ZERO_BF16) || (pdt != ZERO_F16 && pdt != ZERO_BF16))
         return fail(ZERO_EINVAL, "zero_adam_step: grad and param dtypes must be F16 or BF16");
-    if (zero_status hs = zero::check_adamw(*hp, "zero_adam_step"); hs != ZERO_OK)
+    if (zero_status hs = zero::check_adamw(*hp, d_scale == nullptr, "zero_adam_step");
+        hs != ZERO_OK)
         return hs;
     if (n > 0 && (!grad || !master || !exp_avg || !exp_avg_sq || !param_out))
         return fail(ZERO_EINVAL, "zero_adam_step: NULL array with n > 0");
@@ -1052,19 +1109,21 @@ extern "C" zero_status zero_adam_step(const zero_adamw *hp, const void *grad, ze
         return fail(ZERO_EINVAL, "zero_adam_step: n too large");
     if (!aligned(grad, 2) || !aligned(param_out, 2) || !aligned(master, 4) ||
         !aligned(exp_avg, 4) || !aligned(exp_avg_sq, 4) || !aligned(d_state, 8) ||
-        !aligned(d_stats, 8))
+        !aligned(d_stats, 8) || !aligned(d_scale, 8))
         return fail(ZERO_EALIGN, "zero_adam_step: misaligned pointer");
     {
-        const void *buf[7] = {grad, master, exp_avg, exp_avg_sq, param_out, d_state, d_stats};
-        const uint64_t len[7] = {2 * n, 4 * n, 4 * n, 4 * n, 2 * n, sizeof(zero_adam_state_t),
-                                 d_stats ? sizeof(zero_grad_stats_t) : 0};
-        for (int i = 0; i < 7; ++i)
-            for (int j = i + 1; j < 7; ++j)
+        const void *buf[8] = {grad, master, exp_avg, exp_avg_sq, param_out, d_state, d_stats,
+                              d_scale};
+        const uint64_t len[8] = {2 * n, 4 * n, 4 * n, 4 * n, 2 * n, sizeof(zero_adam_state_t),
+                                 d_stats ? sizeof(zero_grad_stats_t) : 0,
+                                 d_scale ? sizeof(zero_loss_scale_t) : 0};
+        for (int i = 0; i < 8; ++i)
+            for (int j = i + 1; j < 8; ++j)
                 if (overlap(buf[i], len[i], buf[j], len[j]))
                     return fail(ZERO_EINVAL, "zero_adam_step: buffers %d and %d overlap", i, j);
     }
     hipStream_t s = (hipStream_t)stream;
-    zero_status st = zero::launch_adam_scalars(*hp, d_stats, d_state, stream);
+    zero_status st = zero::launch_adam_scalars(*hp, d_stats, d_scale, d_state, stream);
     if (st != ZERO_OK || n == 0)
         return st;
 
@@ -1099,4 +1158,36 @@ extern "C" zero_status zero_adam_step(const zero_adamw *hp, const void *grad, ze
     else if (pb) launch_adam<false, true>(a, work, s);
     else launch_adam<false, false>(a, work, s);
     return launch_status("zero_adam_step");
+}
+
+extern "C" zero_status zero_loss_scale_init(const zero_loss_scaler *cfg, zero_loss_scale_t *d_scale,
+                                            void *stream)
+{
+    const char *what = "zero_loss_scale_init";
+    if (!cfg || !d_scale)
+        return fail(ZERO_EINVAL, "%s: NULL argument", what);
+    if (zero_status st = zero::check_scaler(*cfg, what); st != ZERO_OK)
+        return st;
+    if (!aligned(d_scale, 8))
+        return fail(ZERO_EALIGN, "%s: misaligned d_scale", what);
+    hipLaunchKernelGGL(loss_scale_init, dim3(1), dim3(64), 0, (hipStream_t)stream, *cfg, d_scale);
+    return launch_status(what);
+}
+
+extern "C" zero_status zero_loss_scale_update(const zero_loss_scaler *cfg,
+                                              const zero_grad_stats_t *d_stats,
+                                              zero_loss_scale_t *d_scale, void *stream)
+{
+    const char *what = "zero_loss_scale_update";
+    if (!cfg || !d_stats || !d_scale)
+        return fail(ZERO_EINVAL, "%s: NULL argument", what);
+    if (zero_status st = zero::check_scaler(*cfg, what); st != ZERO_OK)
+        return st;
+    if (!aligned(d_scale, 8) || !aligned(d_stats, 8))
+        return fail(ZERO_EALIGN, "%s: misaligned d_stats or d_scale", what);
+    if (overlap(d_scale, sizeof *d_scale, d_stats, sizeof *d_stats))
+        return fail(ZERO_EINVAL, "%s: d_stats and d_scale overlap", what);
+    hipLaunchKernelGGL(loss_scale_update, dim3(1), dim3(64), 0, (hipStream_t)stream, *cfg,
+                       d_stats, d_scale);
+    return launch_status(what);
 }

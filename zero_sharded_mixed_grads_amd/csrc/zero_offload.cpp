@@ -153,6 +153,7 @@ extern "C" zero_status zero_offload_adam_step(const zero_adamw *hp, const void *
                                               float *exp_avg_host, float *exp_avg_sq_host,
                                               void *param_out, zero_dtype pdt, uint64_t n,
                                               const zero_grad_stats_t *d_stats,
+                                              const zero_loss_scale_t *d_scale,
                                               zero_adam_state_t *d_state, void *staging,
                                               size_t staging_bytes, void *stream)
 {
@@ -161,7 +162,7 @@ extern "C" zero_status zero_offload_adam_step(const zero_adamw *hp, const void *
         return fail(ZERO_EINVAL, "%s: NULL hyper-parameters or d_state", what);
     if ((gdt != ZERO_F16 && gdt != ZERO_BF16) || (pdt != ZERO_F16 && pdt != ZERO_BF16))
         return fail(ZERO_EINVAL, "%s: grad and param dtypes must be F16 or BF16", what);
-    if (zero_status hs = zero::check_adamw(*hp, what); hs != ZERO_OK)
+    if (zero_status hs = zero::check_adamw(*hp, d_scale == nullptr, what); hs != ZERO_OK)
         return hs;
     if (n > 0 && (!grad || !master_host || !exp_avg_host || !exp_avg_sq_host || !param_out ||
                   !staging))
@@ -174,7 +175,7 @@ extern "C" zero_status zero_offload_adam_step(const zero_adamw *hp, const void *
                     "slot", what, staging_bytes, (unsigned long long)kMinChunk);
     if (((uintptr_t)grad | (uintptr_t)param_out | (uintptr_t)staging) & 1u ||
         ((uintptr_t)master_host | (uintptr_t)exp_avg_host | (uintptr_t)exp_avg_sq_host) & 3u ||
-        ((uintptr_t)d_state & 7u) || ((uintptr_t)d_stats & 7u))
+        ((uintptr_t)d_state & 7u) || ((uintptr_t)d_stats & 7u) || ((uintptr_t)d_scale & 7u))
         return fail(ZERO_EALIGN, "%s: misaligned pointer", what);
     {
         const uintptr_t host[4] = {(uintptr_t)master_host, (uintptr_t)exp_avg_host,
@@ -184,19 +185,20 @@ extern "C" zero_status zero_offload_adam_step(const zero_adamw *hp, const void *
             for (int j = i + 1; j < 4; ++j)
                 if (len[i] && len[j] && host[i] < host[j] + len[j] && host[j] < host[i] + len[i])
                     return fail(ZERO_EINVAL, "%s: host buffers %d and %d overlap", what, i, j);
-        const uintptr_t dev[4] = {(uintptr_t)grad, (uintptr_t)param_out, (uintptr_t)d_state,
-                                  (uintptr_t)d_stats};
-        const uint64_t dlen[4] = {2 * n, 2 * n, sizeof(zero_adam_state_t),
-                                  d_stats ? sizeof(zero_grad_stats_t) : 0};
-        for (int i = 0; i < 4; ++i)
-            for (int j = i + 1; j < 4; ++j)
+        const uintptr_t dev[5] = {(uintptr_t)grad, (uintptr_t)param_out, (uintptr_t)d_state,
+                                  (uintptr_t)d_stats, (uintptr_t)d_scale};
+        const uint64_t dlen[5] = {2 * n, 2 * n, sizeof(zero_adam_state_t),
+                                  d_stats ? sizeof(zero_grad_stats_t) : 0,
+                                  d_scale ? sizeof(zero_loss_scale_t) : 0};
+        for (int i = 0; i < 5; ++i)
+            for (int j = i + 1; j < 5; ++j)
                 if (dlen[i] && dlen[j] && dev[i] < dev[j] + dlen[j] && dev[j] < dev[i] + dlen[i])
                     return fail(ZERO_EINVAL, "%s: device buffers %d and %d overlap", what, i, j);
     }
     hipStream_t s = (hipStream_t)stream;
 
     // 1. scalars on the device, as on the GPU path, then to the host
-    zero_status st = zero::launch_adam_scalars(*hp, d_stats, d_state, stream);
+    zero_status st = zero::launch_adam_scalars(*hp, d_stats, d_scale, d_state, stream);
     if (st != ZERO_OK)
         return st;
     zero_adam_state_t hs;
