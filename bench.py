@@ -197,6 +197,67 @@ def copy_probe(steps: int):
     print(json.dumps({"copy_probe": res}), flush=True)
 
 
+def configs_sweep(steps: int, warmup: int):
+    """zero_grad_stats and zero_adam_step timed alone on the flat shard of each
+    workload of at least 100M parameters (1.5B at Nd 1, 7.5B rank 3 of 8, 13B
+    at Nd 1, 100B rank 399 of 400), with the 16-bit arrays at the element
+    phase the shard has in the flat layout.  Prints one JSON line."""
+    import torch
+    import zero_sharded_mixed_grads_amd as z
+    from synth import CONFIGS, gen
+    dev = torch.device("cuda:0")
+    out = {}
+    for idx in (2, 3, 4, 5):
+        cfg = CONFIGS[idx]
+        b, e = z.zero_partition(cfg.psi, cfg.nd, cfg.rank)
+        n, ph = e - b, b % 8
+        tdt = gen.torch_dtype(cfg.dtype)
+        gbuf = torch.empty(n + 8, dtype=tdt, device=dev)
+        pbuf = torch.empty(n + 8, dtype=tdt, device=dev)
+        g, p = gbuf[ph:ph + n], pbuf[ph:ph + n]
+        gen.device_fill_normal_(g, cfg.grad_seed(0), cfg.grad_sigma, cfg.loss_scale)
+        master = torch.empty(n, dtype=torch.float32, device=dev)
+        gen.device_fill_normal_(master, cfg.master_seed(), cfg.master_sigma)
+        m = torch.zeros(n, dtype=torch.float32, device=dev)
+        v = torch.zeros(n, dtype=torch.float32, device=dev)
+        stats, state = z.new_grad_stats(dev), z.new_adam_state(dev)
+        ws = z.new_workspace(n, dev)
+        hp = z.adamw(**cfg.hp.__dict__)
+        calls = {
+            "grad_stats": lambda: z.zero_grad_stats(g, cfg.dtype, n, cfg.hp.inv_loss_scale, ws,
+                                                    ws.numel(), stats),
+            "adam_step": lambda: z.zero_adam_step(hp, g, cfg.dtype, master, m, v, p, cfg.dtype,
+                                                  n, stats, state),
+        }
+        res = {"n": n, "dtype": cfg.dtype, "phase16": ph}
+        for name, fn in calls.items():
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            evs = []
+            for _ in range(steps):
+                a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                c.record()
+                evs.append((a, c))
+            torch.cuda.synchronize()
+            ms = sorted(x.elapsed_time(y) for x, y in evs)
+            bpp = ADAM_BYTES_PER_PARAM if name == "adam_step" else STATS_BYTES_PER_PARAM
+            med = ms[len(ms) // 2]
+            res[name] = {"ms_median": med, "ms_min": ms[0], "GB/s": bpp * n / med / 1e6,
+                         "frac": bpp * n / med / 1e6 / HBM_PEAK_GBS}
+        st = z.read_adam_state(state)
+        if st.skip or st.step != warmup + steps:
+            raise SystemExit(f"{cfg.name}: a step was skipped; timing would be invalid")
+        out[cfg.name] = res
+        log(f"[bench] {cfg.name}: n={n} adam {res['adam_step']['ms_median']:.3f} ms "
+            f"({res['adam_step']['GB/s']:.0f} GB/s)")
+        del gbuf, pbuf, g, p, master, m, v, ws
+        torch.cuda.empty_cache()
+    print(json.dumps({"configs": out}), flush=True)
+
+
 def offload_bench(cfg_idx: int, steps: int, warmup: int, chunk: int = 1 << 24):
     """The optimizer step with master/m/v in host memory (zero_offload_adam_step)
     on the same shard: gradients and params on the device, statistics on the
@@ -265,6 +326,8 @@ def main():
                     help="gather per fused buffer, then a separate statistics pass")
     ap.add_argument("--offload", action="store_true",
                     help="time the step with the optimizer state in host memory instead")
+    ap.add_argument("--configs", action="store_true",
+                    help="time grad stats and AdamW alone on every workload of >= 100M params")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one data-parallel rank's shard on one GPU; runs on more "
@@ -276,6 +339,9 @@ def main():
         return
     if args.offload:
         offload_bench(args.config, args.steps, args.warmup)
+        return
+    if args.configs:
+        configs_sweep(args.steps, args.warmup)
         return
 
     import torch

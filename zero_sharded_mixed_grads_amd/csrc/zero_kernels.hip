@@ -210,26 +210,58 @@ __device__ __forceinline__ void store_run(uint16_t *line, const uint32_t *h)
 }
 
 // Eight halves whose first element sits at slot PH of the aligned line
-// `line`: slots PH..7 of this line and 0..PH-1 of the next one.
+// `line` span two lines: slots PH..7 of this line (the head) and slots
+// 0..PH-1 of the next one (the tail).  Each part is written on its own, as
+// naturally aligned pieces, by the lanes that cannot form a whole line.
 template <int PH>
-__device__ __forceinline__ void store_phased(uint16_t *line, const uint32_t *h)
+__device__ __forceinline__ void store_head(uint16_t *line, const uint32_t *h)
 {
     store_run<PH, 8 - PH>(line, h);
-    store_run<0, PH>(line + 8, h + 8 - PH);
 }
 
-__device__ __forceinline__ void store_phased_rt(uint16_t *line, const uint32_t *h, uint32_t ph)
+template <int PH>
+__device__ __forceinline__ void store_tail(uint16_t *next_line, const uint32_t *h)
+{
+    store_run<0, PH>(next_line, h + 8 - PH);
+}
+
+__device__ __forceinline__ void store_head_rt(uint16_t *line, const uint32_t *h, uint32_t ph)
 {
     switch (ph) {
-    case 1: store_phased<1>(line, h); break;
-    case 2: store_phased<2>(line, h); break;
-    case 3: store_phased<3>(line, h); break;
-    case 4: store_phased<4>(line, h); break;
-    case 5: store_phased<5>(line, h); break;
-    case 6: store_phased<6>(line, h); break;
-    case 7: store_phased<7>(line, h); break;
-    default: store_run<0, 8>(line, h); break;
+    case 1: store_head<1>(line, h); break;
+    case 2: store_head<2>(line, h); break;
+    case 3: store_head<3>(line, h); break;
+    case 4: store_head<4>(line, h); break;
+    case 5: store_head<5>(line, h); break;
+    case 6: store_head<6>(line, h); break;
+    default: store_head<7>(line, h); break;
     }
+}
+
+__device__ __forceinline__ void store_tail_rt(uint16_t *next_line, const uint32_t *h, uint32_t ph)
+{
+    switch (ph) {
+    case 1: store_tail<1>(next_line, h); break;
+    case 2: store_tail<2>(next_line, h); break;
+    case 3: store_tail<3>(next_line, h); break;
+    case 4: store_tail<4>(next_line, h); break;
+    case 5: store_tail<5>(next_line, h); break;
+    case 6: store_tail<6>(next_line, h); break;
+    default: store_tail<7>(next_line, h); break;
+    }
+}
+
+// The 16 bytes of lane `lane + d` (d = +1 or -1 within the wave).
+__device__ __forceinline__ uint4 shfl_line_down(const uint4 &x)
+{
+    return make_uint4(__shfl_down(x.x, 1, 64), __shfl_down(x.y, 1, 64), __shfl_down(x.z, 1, 64),
+                      __shfl_down(x.w, 1, 64));
+}
+
+__device__ __forceinline__ uint4 shfl_line_up(const uint4 &x)
+{
+    return make_uint4(__shfl_up(x.x, 1, 64), __shfl_up(x.y, 1, 64), __shfl_up(x.z, 1, 64),
+                      __shfl_up(x.w, 1, 64));
 }
 
 // fp64 wave reduction over 64 lanes (fixed butterfly order).
@@ -612,6 +644,14 @@ __device__ __forceinline__ void adamw_elem(const Coeffs &k, float graw, float &t
 
 constexpr int kAdamUnroll = ZERO_ADAM_UNROLL;
 
+// Whether chunk c's right neighbour c + 1 is not held by the next lane of the
+// same wave: c is on the last lane, or c + 1 is past the body.  Chunks of one
+// unrolled step are consecutive across the lanes of a wave.
+__device__ __forceinline__ bool edge_hi(uint64_t c, uint64_t nchunks)
+{
+    return threadIdx.x % 64 == 63 || c + 1 >= nchunks;
+}
+
 template <bool GBF16, bool PBF16, bool G_ALIGNED, bool P_ALIGNED>
 __global__ void __launch_bounds__(kBlock) adamw_stream(AdamArgs a)
 {
@@ -647,17 +687,19 @@ __global__ void __launch_bounds__(kBlock) adamw_stream(AdamArgs a)
     const uint64_t advance = stride * kAdamUnroll;
 #endif
     for (uint64_t base = first; base < a.nchunks; base += advance) {
-        uint4 gw[kAdamUnroll];
+        uint4 gw[kAdamUnroll], ghi[kAdamUnroll];
         float4 th[kAdamUnroll][2], mm[kAdamUnroll][2], vv[kAdamUnroll][2];
 #pragma unroll
         for (int j = 0; j < kAdamUnroll; ++j) {
             const uint64_t c = base + j * step;
             if (c < a.nchunks) {
-                if constexpr (G_ALIGNED) {
-                    gw[j] = ld_stream(gl + c);
-                } else {
-                    const uint4 lo = ld_stream(gl + c), hi = ld_stream(gl + c + 1);
-                    gw[j] = shift_lines_rt(lo, hi, gsb);
+                gw[j] = ld_stream(gl + c);
+                if constexpr (!G_ALIGNED) {
+                    // the next aligned line is the next lane's own line; only the
+                    // last lane of the wave and the last chunk load it themselves
+                    // (it holds at least one live element, so it is mapped)
+                    if (edge_hi(c, a.nchunks))
+                        ghi[j] = ld_stream(gl + c + 1);
                 }
                 th[j][0] = ld_stream(th4 + 2 * c); th[j][1] = ld_stream(th4 + 2 * c + 1);
                 mm[j][0] = ld_stream(m4 + 2 * c);  mm[j][1] = ld_stream(m4 + 2 * c + 1);
@@ -668,6 +710,10 @@ __global__ void __launch_bounds__(kBlock) adamw_stream(AdamArgs a)
         for (int j = 0; j < kAdamUnroll; ++j) {
             const uint64_t c = base + j * step;
             if (c < a.nchunks) {
+                if constexpr (!G_ALIGNED) {
+                    const uint4 nxt = shfl_line_down(gw[j]);
+                    gw[j] = shift_lines_rt(gw[j], edge_hi(c, a.nchunks) ? ghi[j] : nxt, gsb);
+                }
                 const uint32_t gws[4] = {gw[j].x, gw[j].y, gw[j].z, gw[j].w};
                 float *t = reinterpret_cast<float *>(th[j]);
                 float *mv = reinterpret_cast<float *>(mm[j]);
@@ -683,10 +729,25 @@ __global__ void __launch_bounds__(kBlock) adamw_stream(AdamArgs a)
                 st_stream(th4 + 2 * c, th[j][0]); st_stream(th4 + 2 * c + 1, th[j][1]);
                 st_stream(m4 + 2 * c, mm[j][0]);  st_stream(m4 + 2 * c + 1, mm[j][1]);
                 st_stream(v4 + 2 * c, vv[j][0]);  st_stream(v4 + 2 * c + 1, vv[j][1]);
-                if constexpr (P_ALIGNED)
+                if constexpr (P_ALIGNED) {
                     store_run<0, 8>(pl + 8 * c, ph);
-                else
-                    store_phased_rt(pl + 8 * c, ph, a.p_phase);
+                } else {
+                    // aligned line c holds the previous chunk's last p_phase values
+                    // and this chunk's first 8 - p_phase: every lane but the first
+                    // of the wave takes the former from its left neighbour and
+                    // writes the whole line; the first lane writes only its head,
+                    // and the lane whose right neighbour is absent writes its tail
+                    const uint4 own = make_uint4(ph[0] | ph[1] << 16, ph[2] | ph[3] << 16,
+                                                 ph[4] | ph[5] << 16, ph[6] | ph[7] << 16);
+                    const uint4 prev = shfl_line_up(own);
+                    if (threadIdx.x % 64 != 0)
+                        st_stream(reinterpret_cast<uint4 *>(pl + 8 * c),
+                                  shift_lines_rt(prev, own, 16 - 2 * a.p_phase));
+                    else
+                        store_head_rt(pl + 8 * c, ph, a.p_phase);
+                    if (edge_hi(c, a.nchunks))
+                        store_tail_rt(pl + 8 * c + 8, ph, a.p_phase);
+                }
             }
         }
     }
