@@ -264,12 +264,38 @@ __device__ __forceinline__ uint4 shfl_line_up(const uint4 &x)
                       __shfl_up(x.w, 1, 64));
 }
 
-// fp64 wave reduction over 64 lanes (fixed butterfly order).
+// x moved across lanes by one DPP pattern (both 32-bit halves).  Only the
+// rows in ROW_MASK receive a defined value.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp_moved(double x)
+{
+    const uint64_t u = (uint64_t)__double_as_longlong(x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROW_MASK,
+                                                              0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL,
+                                                              ROW_MASK, 0xF, false);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// fp64 sum over the 64 lanes of a wave in a fixed order, returned to every
+// lane; every lane must be active.  DPP within each 16-lane row (two quad
+// permutes, then the half-row and row mirrors leave the row's sum in all its
+// lanes); then row 1 adds row 0 and row 3 adds row 2 (row_bcast:15, rows 1
+// and 3 only), and row 3 adds row 1 (row_bcast:31, rows 2 and 3), so lane 63
+// holds the total, which is read out.  Rows 0 and 2 end undefined and are
+// never read.  No LDS.
 __device__ __forceinline__ double wave_sum(double x)
 {
-    for (int o = 32; o > 0; o >>= 1)
-        x += __shfl_xor(x, o, 64);
-    return x;
+    x += dpp_moved<0xB1>(x);       // quad_perm [1, 0, 3, 2]
+    x += dpp_moved<0x4E>(x);       // quad_perm [2, 3, 0, 1]
+    x += dpp_moved<0x141>(x);      // row_half_mirror
+    x += dpp_moved<0x140>(x);      // row_mirror
+    x += dpp_moved<0x142, 0xA>(x); // row_bcast:15 into rows 1 and 3
+    x += dpp_moved<0x143, 0xC>(x); // row_bcast:31 into rows 2 and 3
+    const uint64_t u = (uint64_t)__double_as_longlong(x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
 // ================================================================ flatten
