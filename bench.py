@@ -40,7 +40,15 @@ KERNEL_SRC = os.path.join(ROOT, "zero_sharded_mixed_grads_amd", "csrc", "zero_ke
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the kernel source's code: line comments, trailing blanks and
+    empty lines are dropped, so that editing comments keeps the stored
+    counter results valid while any change to the code invalidates them."""
+    code = []
+    for line in open(KERNEL_SRC, encoding="utf-8"):
+        line = line.split("//", 1)[0].rstrip()
+        if line:
+            code.append(line)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def log(*a):

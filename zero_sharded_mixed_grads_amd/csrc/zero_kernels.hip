@@ -1,28 +1,34 @@
 // Device path of libzero_mi355x for AMD MI355X (gfx950, CDNA4, wave64).
 //
-// Three HBM-bound streaming kernels and two single-block epilogues:
+// Three HBM-bound streaming kernels and one-thread / one-block epilogues:
 //   flatten_segments  - list-order gather of tensors into a contiguous buffer
 //                       ("ZeRO: Memory Optimizations Toward Training Trillion
 //                       Parameter Models", paper summary page, section ZeRO-R
-//                       > CB: constant-size fused buffers)
-//   stats_pass1/2     - overflow flag and fp64 squared norm of a 16-bit
-//                       gradient shard, fixed-order two-pass reduction
+//                       > CB: constant-size fused buffers); in its statistics
+//                       modes it also sums the squares of what it writes
+//   stats_pass1, stats_reduce, stats_final
+//                     - overflow flag and fp64 squared norm of a 16-bit
+//                       gradient shard, fixed-order reduction of per-tile sums
 //   adam_scalars      - per-step scalars in fp64 (skip, clip, bias corrections)
 //   adamw_stream      - the fused AdamW update of one rank's shard (same page,
 //                       section ZeRO-DP, Stage 1: each rank updates only its
 //                       1/Nd of the optimizer state; section メモリ消費の定量化:
 //                       16-bit params and grads, fp32 master, momentum and
-//                       variance), 28 bytes of HBM traffic per element.
+//                       variance), 28 bytes of HBM traffic per element
+//   loss_scale_init, loss_scale_update
+//                     - the device-resident dynamic loss scale (Micikevicius
+//                       et al., "Mixed Precision Training")
 //
 // Memory access rules used throughout: every global load and store is
 // naturally aligned (16-byte vectors on 16-byte boundaries, dwords on 4,
 // shorts on 2).  A 16-bit stream whose 16-byte phase differs from the fp32
-// streams is realigned in registers: loads read the two aligned 16-byte lines
-// that cover the 8 wanted elements and funnel-shift them with v_alignbyte;
-// stores split the 8 elements into naturally aligned pieces.  An aligned line
-// that holds at least one byte of a live buffer lies inside a mapped page, so
-// the over-read of such a line never faults; over-read bytes are discarded.
-// No scalar-cache writes, no float atomics: results are bit-reproducible.
+// streams is realigned in registers: the 8 wanted elements are funnel-shifted
+// out of two aligned 16-byte lines (v_alignbyte), and stores are assembled
+// into whole aligned lines with the neighbouring lane's values, or split into
+// naturally aligned pieces at the edges.  An aligned line that holds at least
+// one byte of a live buffer lies inside a mapped page, so the over-read of
+// such a line never faults; over-read bytes are discarded.  Reductions run in
+// a fixed order and there are no atomics: results are bit-reproducible.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
