@@ -55,8 +55,41 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+POOL_CAP = 200 << 30    # bytes: the widest pool the state arrays are spread over
+POOL_MARGIN = 8 << 30  # bytes of device memory left free beside the pool
+
+
+def state_arrays(n: int, dt16, device, spread: bool = True):
+    """The five state arrays of an n-element shard (16-bit grad, fp32 master,
+    m, v, 16-bit param).  spread: views of one pool, placed by
+    zero_state_layout (as far apart as the pool allows; AdamW streams the five
+    at once and runs fastest when they lie far apart in HBM).  The pool takes
+    the free device memory, capped at POOL_CAP and leaving POOL_MARGIN free;
+    if it cannot hold the arrays apart, or spread is False, they are separate
+    allocations.  Returns the arrays and a description of the layout."""
+    import torch
+    import zero_sharded_mixed_grads_amd as z
+    sizes = (2 * n, 4 * n, 4 * n, 4 * n, 2 * n)
+    dts = (dt16, torch.float32, torch.float32, torch.float32, dt16)
+    if spread:
+        free, _ = torch.cuda.mem_get_info(device)
+        pool_bytes = min(POOL_CAP, free - POOL_MARGIN) // (2 << 20) * (2 << 20)
+        try:
+            offs = z.zero_state_layout(n, pool_bytes)
+        except z.ZeroError:
+            offs = None
+        if offs is not None:
+            pool = torch.empty(pool_bytes, dtype=torch.uint8, device=device)
+            arrays = [pool[o:o + nb].view(dt) for o, nb, dt in zip(offs, sizes, dts)]
+            return (*arrays, {"kind": "spread", "pool_bytes": pool_bytes,
+                              "spacing_bytes": offs[1]})
+    arrays = [torch.empty(nb // (2 if dt != torch.float32 else 4), dtype=dt, device=device)
+              for nb, dt in zip(sizes, dts)]
+    return (*arrays, {"kind": "separate"})
+
+
 class Workload:
-    def __init__(self, cfg_idx: int, device):
+    def __init__(self, cfg_idx: int, device, spread: bool = True):
         import torch
         import zero_sharded_mixed_grads_amd as z
         from synth import CONFIGS, gen
@@ -78,12 +111,12 @@ class Workload:
             gen.device_fill_normal_(t, cfg.grad_seed(0) * 100003 + i, cfg.grad_sigma,
                                     cfg.loss_scale)
             self.grads[i] = t
-        self.g = torch.empty(n, dtype=tdt, device=device)          # flat grad shard
-        self.master = torch.empty(n, dtype=torch.float32, device=device)
+        # the five state arrays: flat grad shard, master, m, v, param shard
+        self.g, self.master, self.m, self.v, self.p, self.layout = state_arrays(
+            n, tdt, device, spread)
         gen.device_fill_normal_(self.master, cfg.master_seed(), cfg.master_sigma)
-        self.m = torch.zeros(n, dtype=torch.float32, device=device)
-        self.v = torch.zeros(n, dtype=torch.float32, device=device)
-        self.p = torch.empty(n, dtype=tdt, device=device)
+        self.m.zero_()
+        self.v.zero_()
         self.stats = z.new_grad_stats(device)
         self.state = z.new_adam_state(device)
         self.ws = z.new_workspace(n, device)
@@ -205,7 +238,7 @@ def copy_probe(steps: int):
     print(json.dumps({"copy_probe": res}), flush=True)
 
 
-def configs_sweep(steps: int, warmup: int):
+def configs_sweep(steps: int, warmup: int, spread: bool = True):
     """zero_grad_stats and zero_adam_step timed alone on the flat shard of each
     workload of at least 100M parameters (1.5B at Nd 1, 7.5B rank 3 of 8, 13B
     at Nd 1, 100B rank 399 of 400), with the 16-bit arrays at the element
@@ -220,14 +253,13 @@ def configs_sweep(steps: int, warmup: int):
         b, e = z.zero_partition(cfg.psi, cfg.nd, cfg.rank)
         n, ph = e - b, b % 8
         tdt = gen.torch_dtype(cfg.dtype)
-        gbuf = torch.empty(n + 8, dtype=tdt, device=dev)
-        pbuf = torch.empty(n + 8, dtype=tdt, device=dev)
+        gbuf, master, m, v, pbuf, layout = state_arrays(n + 8, tdt, dev, spread)
         g, p = gbuf[ph:ph + n], pbuf[ph:ph + n]
+        master, m, v = master[:n], m[:n], v[:n]
         gen.device_fill_normal_(g, cfg.grad_seed(0), cfg.grad_sigma, cfg.loss_scale)
-        master = torch.empty(n, dtype=torch.float32, device=dev)
         gen.device_fill_normal_(master, cfg.master_seed(), cfg.master_sigma)
-        m = torch.zeros(n, dtype=torch.float32, device=dev)
-        v = torch.zeros(n, dtype=torch.float32, device=dev)
+        m.zero_()
+        v.zero_()
         stats, state = z.new_grad_stats(dev), z.new_adam_state(dev)
         ws = z.new_workspace(n, dev)
         hp = z.adamw(**cfg.hp.__dict__)
@@ -237,7 +269,7 @@ def configs_sweep(steps: int, warmup: int):
             "adam_step": lambda: z.zero_adam_step(hp, g, cfg.dtype, master, m, v, p, cfg.dtype,
                                                   n, stats, state),
         }
-        res = {"n": n, "dtype": cfg.dtype, "phase16": ph}
+        res = {"n": n, "dtype": cfg.dtype, "phase16": ph, "state_layout": layout}
         for name, fn in calls.items():
             for _ in range(warmup):
                 fn()
@@ -261,7 +293,7 @@ def configs_sweep(steps: int, warmup: int):
         out[cfg.name] = res
         log(f"[bench] {cfg.name}: n={n} adam {res['adam_step']['ms_median']:.3f} ms "
             f"({res['adam_step']['GB/s']:.0f} GB/s)")
-        del gbuf, pbuf, g, p, master, m, v, ws
+        del gbuf, pbuf, g, p, master, m, v, ws, calls
         torch.cuda.empty_cache()
     print(json.dumps({"configs": out}), flush=True)
 
@@ -334,6 +366,9 @@ def main():
                     help="gather per fused buffer, then a separate statistics pass")
     ap.add_argument("--offload", action="store_true",
                     help="time the step with the optimizer state in host memory instead")
+    ap.add_argument("--separate", action="store_true",
+                    help="allocate the five state arrays separately instead of spreading "
+                         "them over one pool")
     ap.add_argument("--configs", action="store_true",
                     help="time grad stats and AdamW alone on every workload of >= 100M params")
     args = ap.parse_args()
@@ -349,13 +384,13 @@ def main():
         offload_bench(args.config, args.steps, args.warmup)
         return
     if args.configs:
-        configs_sweep(args.steps, args.warmup)
+        configs_sweep(args.steps, args.warmup, spread=not args.separate)
         return
 
     import torch
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = Workload(args.config, dev)
+    w = Workload(args.config, dev, spread=not args.separate)
 
     fused = not args.unfused
     for _ in range(args.warmup):
@@ -422,7 +457,7 @@ def main():
                    "nd": w.cfg.nd, "rank": w.cfg.rank, "shard_params": n,
                    "grad_dtype": w.cfg.dtype, "param_dtype": w.cfg.dtype,
                    "bucket_elems": w.cfg.bucket_elems, "max_grad_norm": w.cfg.hp.max_grad_norm,
-                   "loss_scale": w.cfg.loss_scale},
+                   "loss_scale": w.cfg.loss_scale, "state_layout": w.layout},
         "roofline": {"bound": "hbm", "achieved": adam_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": adam_gbs / HBM_PEAK_GBS, "traffic": traffic},
         "kernels": kernels,

@@ -113,6 +113,22 @@ zero_status zero_bucket_plan(const uint64_t *numel, uint32_t n_tensors, uint64_t
                              uint64_t range_begin, uint64_t range_end, zero_segment *segs,
                              uint64_t cap, uint64_t *n_segs);
 
+/* Where to put one rank's five state arrays inside one caller-allocated
+ * device pool of pool_bytes bytes, for bandwidth.  The arrays are, in this
+ * order: grad (n 16-bit values), master, exp_avg, exp_avg_sq (n fp32 each),
+ * param (n 16-bit values).  ([P2] ZeRO-R, MD: model states go to
+ * pre-allocated contiguous regions.  The pages say nothing about where in
+ * HBM; the layout is this library's.)  On MI355X, AdamW streams the five
+ * arrays at once and runs about 15% faster when they lie far apart in HBM:
+ * measured on the 1.5B shard, 5.28 TB/s with separate allocations against
+ * 6.04 TB/s spread over a 100 GB pool and 6.08 TB/s over 200 GB.  The arrays
+ * are therefore spread evenly: offsets[i] = i * step, with step a multiple of
+ * 2 MiB and 4 * step + 2n + 16 <= pool_bytes, so every array may also be
+ * shifted by up to 16 bytes (a 16-bit shard's phase in its flat buffer).
+ * Errors: ZERO_EINVAL (NULL offsets, n too large), ZERO_ENOSPC (the pool is
+ * too small for non-overlapping arrays: step < 4n + 16). */
+zero_status zero_state_layout(uint64_t n, uint64_t pool_bytes, uint64_t offsets[5]);
+
 /* ------------------------------------------------------------ device calls */
 
 /* [P2] ZeRO-R, CB and MD: copies elements [range_begin, range_begin + count)

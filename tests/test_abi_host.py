@@ -23,7 +23,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     assert set(names) == set(z.EXPORTS)
     L = ctypes.CDLL(z.LIB_PATH)
     for name in names:
@@ -310,3 +310,28 @@ def test_loss_scale_validation_on_host():
                    None, stt, 0, h[1] + 64) == z.ZERO_EINVAL  # d_scale inside master
     assert _status(z.zero_adam_step, z.adamw(), h[0], "f16", h[1], h[2], h[3], h[4], "f16", n,
                    None, stt, 0, d + 4) == z.ZERO_EALIGN
+
+
+def test_state_layout():
+    """Five arrays (2n, 4n, 4n, 4n, 2n bytes) evenly spread over the pool:
+    2 MiB aligned starts, no overlap even with a 16-byte phase shift, inside
+    the pool, and the widest such spacing; too small a pool is rejected."""
+    MiB = 1 << 20
+    sizes = lambda n: [2 * n, 4 * n, 4 * n, 4 * n, 2 * n]
+    for n, pool in ((1_557_611_200, 200 << 30), (1_557_611_200, 100 << 30), (1000, 64 * MiB),
+                    (250_728_263, 40 << 30), (1, 9 * MiB)):
+        offs = z.zero_state_layout(n, pool)
+        step = offs[1]
+        assert offs == [i * step for i in range(5)] and step % (2 * MiB) == 0
+        for o, o_next, sz in zip(offs, offs[1:], sizes(n)):
+            assert o + sz + 16 <= o_next
+        assert offs[4] + 2 * n + 16 <= pool
+        assert 4 * (step + 2 * MiB) + 2 * n + 16 > pool  # no wider step fits
+    n = 1 << 20
+    with pytest.raises(z.ZeroError) as e:
+        z.zero_state_layout(n, 18 * n)
+    assert e.value.status == z.ZERO_ENOSPC and "at least" in str(e.value)
+    need = int(str(e.value).rsplit("at least ", 1)[1].rstrip(")"))
+    assert z.zero_state_layout(n, need)[1] >= 4 * n + 16
+    with pytest.raises(z.ZeroError):
+        z.zero_state_layout(n, need - 1)

@@ -79,7 +79,7 @@ EXPORTS = ("zero_status_str", "zero_last_error", "zero_partition", "zero_mem_byt
            "zero_grad_stats", "zero_bucket_flatten_stats_workspace", "zero_bucket_flatten_stats",
            "zero_adam_step", "zero_offload_staging_bytes", "zero_offload_adam_step",
            "zero_ckpt_save", "zero_ckpt_read_header", "zero_ckpt_load",
-           "zero_loss_scale_init", "zero_loss_scale_update")
+           "zero_loss_scale_init", "zero_loss_scale_update", "zero_state_layout")
 
 _lib = None
 
@@ -113,6 +113,7 @@ def lib():
         L.zero_adam_step.argtypes = [ctypes.POINTER(AdamW), VP, ctypes.c_int, VP, VP, VP, VP,
                                      ctypes.c_int, U64, VP, VP, VP, VP]
         L.zero_loss_scale_init.argtypes = [ctypes.POINTER(LossScaler), VP, VP]
+        L.zero_state_layout.argtypes = [U64, U64, ctypes.POINTER(U64)]
         L.zero_loss_scale_update.argtypes = [ctypes.POINTER(LossScaler), VP, VP, VP]
         L.zero_offload_staging_bytes.argtypes = [U64, ctypes.POINTER(ctypes.c_size_t)]
         L.zero_offload_adam_step.argtypes = [ctypes.POINTER(AdamW), VP, ctypes.c_int, VP, VP,
@@ -185,6 +186,14 @@ def zero_bucket_plan(numel: Sequence[int], bucket_elems: int, range_begin: int,
     _check(lib().zero_bucket_plan(arr, len(numel), bucket_elems, range_begin, range_end,
                                   segs, cap, ctypes.byref(n)))
     return [(s.bucket, s.tensor, s.src_off, s.dst_off, s.len) for s in segs[:n.value]]
+
+
+def zero_state_layout(n: int, pool_bytes: int) -> List[int]:
+    """Byte offsets of grad, master, exp_avg, exp_avg_sq and param inside one
+    device pool, spread evenly over it."""
+    out = (U64 * 5)()
+    _check(lib().zero_state_layout(n, pool_bytes, out))
+    return list(out)
 
 
 # ------------------------------------------------------------- device calls

@@ -174,3 +174,24 @@ extern "C" zero_status zero_bucket_plan(const uint64_t *numel, uint32_t n_tensor
                     (unsigned long long)count, (unsigned long long)cap);
     return ZERO_OK;
 }
+
+extern "C" zero_status zero_state_layout(uint64_t n, uint64_t pool_bytes, uint64_t offsets[5])
+{
+    if (!offsets)
+        return fail(ZERO_EINVAL, "zero_state_layout: NULL offsets");
+    if (n > (UINT64_MAX >> 5))
+        return fail(ZERO_EINVAL, "zero_state_layout: n too large");
+    constexpr uint64_t kAlign = 2ull << 20;  // 2 MiB
+    const uint64_t need_tail = 2 * n + 16;   // the param array, plus room for its phase
+    const uint64_t min_step = 4 * n + 16;    // the largest of the first four, plus phase
+    uint64_t step = pool_bytes > need_tail ? (pool_bytes - need_tail) / 4 / kAlign * kAlign : 0;
+    if (step < min_step)
+        return fail(ZERO_ENOSPC, "zero_state_layout: a pool of %llu bytes cannot hold five "
+                    "non-overlapping arrays of %llu elements (needs at least %llu)",
+                    (unsigned long long)pool_bytes, (unsigned long long)n,
+                    (unsigned long long)(4 * ((min_step + kAlign - 1) / kAlign * kAlign) +
+                                         need_tail));
+    for (int i = 0; i < 5; ++i)
+        offsets[i] = (uint64_t)i * step;
+    return ZERO_OK;
+}
