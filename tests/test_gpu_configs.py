@@ -65,19 +65,30 @@ def _sample_indices(cfg, begin, end, n_random, seed, bucket=None):
 class Rank:
     """Device state of one rank's shard plus the calls of one step."""
 
-    def __init__(self, cfg, p_phase=0, grads_list=True):
+    def __init__(self, cfg, p_phase=0, grads_list=True, spread=False):
+        """spread: the five state arrays are placed in one pool exactly as the
+        benchmark places them (zero_state_layout); otherwise separate tensors."""
         self.cfg = cfg
         self.begin, self.end = z.zero_partition(cfg.psi, cfg.nd, cfg.rank)
         assert (self.begin, self.end) == oracle.partition(cfg.psi, cfg.nd, cfg.rank)
         n = self.n = self.end - self.begin
         d = dev()
         tdt = gen.torch_dtype(cfg.dtype)
-        self.g = torch.empty(n, dtype=tdt, device=d)
-        self.master = torch.empty(n, dtype=torch.float32, device=d)
-        self.m = torch.zeros(n, dtype=torch.float32, device=d)
-        self.v = torch.zeros(n, dtype=torch.float32, device=d)
+        if spread:
+            import bench
+            g, master, m, v, self.p_raw, self.layout = bench.state_arrays(n + 8, tdt, d)
+            assert self.layout["kind"] == "spread", self.layout
+            self.g, self.master, self.m, self.v = g[:n], master[:n], m[:n], v[:n]
+            self.m.zero_()
+            self.v.zero_()
+            self.p_raw.zero_()
+        else:
+            self.g = torch.empty(n, dtype=tdt, device=d)
+            self.master = torch.empty(n, dtype=torch.float32, device=d)
+            self.m = torch.zeros(n, dtype=torch.float32, device=d)
+            self.v = torch.zeros(n, dtype=torch.float32, device=d)
+            self.p_raw = torch.zeros(n + 8, dtype=tdt, device=d)
         # the 16-bit param shard keeps the phase it has in the full flat buffer
-        self.p_raw = torch.zeros(n + 8, dtype=tdt, device=d)
         self.p = self.p_raw[p_phase:p_phase + n]
         self.stats = z.new_grad_stats(d)
         self.state = z.new_adam_state(d)
@@ -349,10 +360,11 @@ def _run_sampled(cfg, r, idx, fill_grads, label, fused=False):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("fused", [True, False])
 def test_workload2_gpt2_1p5b_sampled(fused):
-    """The bench's workload and launch configuration (fused: the bench's
-    default step; unfused: one gather per 500M-element buffer, then stats)."""
+    """The bench's workload, launch configuration and state layout (fused:
+    the bench's default step; unfused: one gather per 500M-element buffer,
+    then stats)."""
     cfg = CONFIGS[2]
-    r = Rank(cfg)
+    r = Rank(cfg, spread=True)
     assert r.n == cfg.psi == 1_557_611_200
     gen.device_fill_normal_(r.master, cfg.master_seed(), cfg.master_sigma)
     idx = _sample_indices(cfg, r.begin, r.end, 4_000_000, 4242, cfg.bucket_elems)
