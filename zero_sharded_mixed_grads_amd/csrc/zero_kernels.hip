@@ -46,69 +46,27 @@ namespace {
 #endif
 constexpr int kBlock = ZERO_BLOCK;  // threads per block (waves of 64 lanes)
 
-// Tuning knobs of the streaming kernels (compile-time).
+// Tuning constants of the streaming kernels (compile-time; the values are the
+// measured best on the 1.5B shard).
 #ifndef ZERO_ADAM_UNROLL
 #define ZERO_ADAM_UNROLL 2   // 8-element chunks per lane kept in flight
-#endif
-#ifndef ZERO_NT_STORE
-#define ZERO_NT_STORE 0      // 1: non-temporal hint on the AdamW body stores
-#endif
-#ifndef ZERO_NT_LOAD
-#define ZERO_NT_LOAD 0       // 1: non-temporal hint on the AdamW body loads
-#endif
-#ifndef ZERO_BLOCKS_PER_CU
-#define ZERO_BLOCKS_PER_CU 0 // 0: as many as the occupancy calculator allows
-#endif
-#ifndef ZERO_FAST_SQRT_RCP
-#define ZERO_FAST_SQRT_RCP 0 // 1: hardware v_sqrt_f32 / v_rcp_f32 (about 1 ulp each)
-#endif
-#ifndef ZERO_ADAM_MAPPING
-#define ZERO_ADAM_MAPPING 2  // 0: persistent grid-stride chunks; 1: persistent grid-stride
-                             // over contiguous tiles; 2: one contiguous tile per block
-#endif
-#ifndef ZERO_XCD_ORDER
-#define ZERO_XCD_ORDER 1     // 1 (with one tile per block): block i runs on XCD i % 8, so
-                             // tiles are renumbered to give each XCD a contiguous eighth
 #endif
 #ifndef ZERO_FLAT_CPT
 #define ZERO_FLAT_CPT 1      // 16-byte lines per thread in a flatten tile
 #endif
-#ifndef ZERO_FLAT_ONESHOT
-#define ZERO_FLAT_ONESHOT 1  // 1: one flatten tile per block instead of a resident grid
-#endif
 
-// Native vector types behind HIP's vector structs (the non-temporal builtins
-// take scalars or native vectors only).
-template <typename T> struct native { using type = T; };
-template <> struct native<uint4> { using type = unsigned int __attribute__((ext_vector_type(4))); };
-template <> struct native<uint2> { using type = unsigned int __attribute__((ext_vector_type(2))); };
-template <> struct native<float4> { using type = float __attribute__((ext_vector_type(4))); };
-
+// Plain global accesses of the streaming kernels (non-temporal hints were
+// measured slower on this part).
 template <typename T>
 __device__ __forceinline__ T ld_stream(const T *p)
 {
-#if ZERO_NT_LOAD
-    using N = typename native<T>::type;
-    const N x = __builtin_nontemporal_load(reinterpret_cast<const N *>(p));
-    T v;
-    __builtin_memcpy(&v, &x, sizeof v);
-    return v;
-#else
     return *p;
-#endif
 }
 
 template <typename T>
 __device__ __forceinline__ void st_stream(T *p, const T &v)
 {
-#if ZERO_NT_STORE
-    using N = typename native<T>::type;
-    N x;
-    __builtin_memcpy(&x, &v, sizeof v);
-    __builtin_nontemporal_store(x, reinterpret_cast<N *>(p));
-#else
     *p = v;
-#endif
 }
 
 // ------------------------------------------------------------ 16-bit helpers
@@ -661,13 +619,8 @@ __device__ __forceinline__ void adamw_elem(const Coeffs &k, float graw, float &t
     const float g = graw * k.grad_mult;
     const float m1 = fmaf(k.b1, m, k.omb1 * g);
     const float v1 = fmaf(k.b2, v, (k.omb2 * g) * g);
-#if ZERO_FAST_SQRT_RCP
-    const float den = fmaf(__builtin_amdgcn_sqrtf(v1), k.inv_sqrt_bc2, k.eps);
-    const float ratio = m1 * __builtin_amdgcn_rcpf(den);
-#else
-    const float den = fmaf(sqrtf(v1), k.inv_sqrt_bc2, k.eps);
-    const float ratio = m1 / den;
-#endif
+    const float den = fmaf(sqrtf(v1), k.inv_sqrt_bc2, k.eps);  // correctly rounded
+    const float ratio = m1 / den;                              // correctly rounded
     const float th1 = fmaf(-k.decay, th, th);
     th = fmaf(-k.step_size, ratio, th1);
     m = m1;
@@ -701,23 +654,16 @@ __global__ void __launch_bounds__(kBlock) adamw_stream(AdamArgs a)
     uint16_t *pl = a.p + a.head - a.p_phase;  // aligned line holding element `head`
     const uint32_t gsb = 2 * a.g_phase;
 
+    // One contiguous tile of kBlock * kAdamUnroll chunks per block.  Block i
+    // runs on XCD i % 8, so tiles are renumbered to give each XCD (with its own
+    // L2) a contiguous eighth of the shard.  Chunk j of a lane is base + j * step;
+    // the loop takes a second round only if the grid was capped.
     const uint64_t stride = (uint64_t)gridDim.x * kBlock;
-    // chunk j of a lane's group: base + j * step
-#if ZERO_ADAM_MAPPING == 0
-    const uint64_t step = stride;
-    const uint64_t first = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
-    const uint64_t advance = stride * kAdamUnroll;
-#else
     const uint64_t step = kBlock;
-#if ZERO_ADAM_MAPPING == 2 && ZERO_XCD_ORDER
     const uint64_t per_xcd = (gridDim.x + 7) / 8;
     const uint64_t tile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-#else
-    const uint64_t tile = blockIdx.x;
-#endif
     const uint64_t first = tile * kBlock * kAdamUnroll + threadIdx.x;
     const uint64_t advance = stride * kAdamUnroll;
-#endif
     for (uint64_t base = first; base < a.nchunks; base += advance) {
         uint4 gw[kAdamUnroll], ghi[kAdamUnroll];
         float4 th[kAdamUnroll][2], mm[kAdamUnroll][2], vv[kAdamUnroll][2];
@@ -831,10 +777,8 @@ uint32_t resident_blocks(K kernel)
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
         cus = 256;
-    if (ZERO_BLOCKS_PER_CU > 0)
-        per_cu = ZERO_BLOCKS_PER_CU;
-    else if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0) !=
-                 hipSuccess || per_cu <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0) != hipSuccess ||
+        per_cu <= 0)
         per_cu = 4;
     v = (uint32_t)(cus * per_cu);
     cache[dev].store(v, std::memory_order_relaxed);
@@ -852,12 +796,8 @@ inline uint32_t grid_for(uint64_t work_items, uint64_t per_block, uint32_t max_b
 template <int ES, int MODE>
 zero_status flatten_launch(FlatArgs &a, hipStream_t stream)
 {
-#if ZERO_FLAT_ONESHOT
+    // one tile per block; the kernel's tile loop covers a capped grid
     const uint32_t grid = grid_for(a.tile_lo[a.n_segs], 1, 0x7ffffff0u);
-#else
-    const uint32_t grid =
-        grid_for(a.tile_lo[a.n_segs], 1, resident_blocks(flatten_segments<ES, MODE>));
-#endif
     hipLaunchKernelGGL((flatten_segments<ES, MODE>), dim3(grid), dim3(kBlock), 0, stream, a);
     return launch_status("zero_bucket_flatten");
 }
@@ -1155,17 +1095,11 @@ void launch_adam_variant(const AdamArgs &a, uint64_t work, hipStream_t s)
 {
     auto kernel = adamw_stream<GB, PB, GA, PA>;
     const uint64_t per_block = (uint64_t)kBlock * kAdamUnroll;
-#if ZERO_ADAM_MAPPING == 2
     // one tile per block; the element-wise fallback keeps a resident grid
     uint32_t grid = a.nchunks ? grid_for(a.nchunks, per_block, 0x7ffffff0u)
                               : grid_for(work, per_block, resident_blocks(kernel));
-#if ZERO_XCD_ORDER
     if (a.nchunks)
         grid = (grid + 7) / 8 * 8;  // whole rounds of the 8 XCDs; spare blocks find no tile
-#endif
-#else
-    const uint32_t grid = grid_for(work, per_block, resident_blocks(kernel));
-#endif
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), 0, s, a);
 }
 
