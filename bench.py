@@ -78,8 +78,13 @@ def state_arrays(n: int, dt16, device, spread: bool = True):
             offs = z.zero_state_layout(n, pool_bytes)
         except z.ZeroError:
             offs = None
+        pool = None
         if offs is not None:
-            pool = torch.empty(pool_bytes, dtype=torch.uint8, device=device)
+            try:
+                pool = torch.empty(pool_bytes, dtype=torch.uint8, device=device)
+            except torch.OutOfMemoryError:
+                log(f"[bench] no {pool_bytes} B pool available; separate allocations")
+        if pool is not None:
             arrays = [pool[o:o + nb].view(dt) for o, nb, dt in zip(offs, sizes, dts)]
             return (*arrays, {"kind": "spread", "pool_bytes": pool_bytes,
                               "spacing_bytes": offs[1]})
