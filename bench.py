@@ -303,6 +303,60 @@ def configs_sweep(steps: int, warmup: int, spread: bool = True):
     print(json.dumps({"configs": out}), flush=True)
 
 
+def ckpt_bench(cfg_idx: int = 5, reps: int = 2):
+    """Checkpoint save and load of one rank's optimizer state (fp32 master, m,
+    v) to the local temporary directory: save, then load into fresh arrays and
+    compare bit for bit.  The state has the size of the 100B model's rank 399
+    of 400 (250,728,263 params, 3.0 GB); it is saved as the single shard of a
+    run of that size (Nd = 1), because a load needs every shard of a save and
+    400 such files do not fit a local disk.  Prints one JSON line."""
+    import shutil
+    import tempfile
+    import torch
+    import zero_sharded_mixed_grads_amd as z
+    from synth import CONFIGS, gen
+    cfg = CONFIGS[cfg_idx]
+    dev = torch.device("cuda:0")
+    b, e = z.zero_partition(cfg.psi, cfg.nd, cfg.rank)
+    n = e - b
+    tmp = tempfile.mkdtemp(prefix="zero_ckpt_")
+    need = 12 * n + 64
+    if shutil.disk_usage(tmp).free < 2 * need:
+        shutil.rmtree(tmp)
+        print(json.dumps({"ckpt": {"skipped": f"less than {2 * need} bytes free in {tmp}"}}))
+        return
+    src = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(3)]
+    for i, t in enumerate(src):
+        gen.device_fill_normal_(t, cfg.master_seed() + i, 0.02)
+    state = z.new_adam_state(dev)
+    dst = [torch.empty_like(t) for t in src]
+    state2 = z.new_adam_state(dev)
+    path = os.path.join(tmp, "shard.zck")
+    save_s, load_s = [], []
+    try:
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            z.zero_ckpt_save(path, n, 1, 0, *src, state)
+            save_s.append(time.perf_counter() - t0)
+            t0 = time.perf_counter()
+            z.zero_ckpt_load([path], n, 1, 0, *dst, state2)
+            load_s.append(time.perf_counter() - t0)
+        same = all(torch.equal(a.view(torch.int32), c.view(torch.int32))
+                   for a, c in zip(src, dst))
+    finally:
+        shutil.rmtree(tmp)
+    if not same:
+        raise SystemExit("checkpoint round trip changed the state")
+    by = 12 * n
+    print(json.dumps({"ckpt": {"workload": f"{cfg.name} state as one shard",
+                               "shard_params": n, "bytes": by,
+                               "save_s": min(save_s), "load_s": min(load_s),
+                               "save_GB/s": by / min(save_s) / 1e9,
+                               "load_GB/s": by / min(load_s) / 1e9,
+                               "round_trip_bit_exact": same}}), flush=True)
+
+
 def offload_bench(cfg_idx: int, steps: int, warmup: int, chunk: int = 1 << 24):
     """The optimizer step with master/m/v in host memory (zero_offload_adam_step)
     on the same shard: gradients and params on the device, statistics on the
@@ -371,6 +425,8 @@ def main():
                     help="gather per fused buffer, then a separate statistics pass")
     ap.add_argument("--offload", action="store_true",
                     help="time the step with the optimizer state in host memory instead")
+    ap.add_argument("--ckpt", action="store_true",
+                    help="time a sharded checkpoint save and load of one rank's state instead")
     ap.add_argument("--separate", action="store_true",
                     help="allocate the five state arrays separately instead of spreading "
                          "them over one pool")
@@ -387,6 +443,9 @@ def main():
         return
     if args.offload:
         offload_bench(args.config, args.steps, args.warmup)
+        return
+    if args.ckpt:
+        ckpt_bench()
         return
     if args.configs:
         configs_sweep(args.steps, args.warmup, spread=not args.separate)
