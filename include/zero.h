@@ -351,7 +351,7 @@ typedef struct {
     uint64_t begin;    /* this rank's range [begin, end) of the flat vector */
     uint64_t end;
     uint64_t step;     /* device step counter when saved */
-    uint64_t reserved; /* zero */
+    uint64_t flags;    /* bit 0: a 32-byte zero_loss_scale_t follows the arrays */
 } zero_ckpt_header;
 
 /* ("ZeRO" AI-library tutorial page, section "Checkpoint 与恢复": with sharded
@@ -359,18 +359,22 @@ typedef struct {
  * files carry the metadata a resume needs.)  Writes rank `rank`'s optimizer
  * state of a psi-parameter model split over nd ranks to `path`: the header,
  * then the n = end - begin fp32 master, exp_avg and exp_avg_sq values
- * (device arrays of the rank's shard, in that order).  The 16-bit params are
- * not stored: they are the rounding of the master.  Synchronises `stream`
- * first, so pending updates are included; the file appears under `path`
- * only once complete (written to "<path>.tmp", flushed, renamed).
+ * (device arrays of the rank's shard, in that order), then, when d_scale is
+ * not NULL, the 32-byte device loss-scale state (flags bit 0), so that a run
+ * with dynamic loss scaling resumes exactly.  The 16-bit params are not
+ * stored: they are the rounding of the master.  Synchronises `stream` first,
+ * so pending updates are included; the file appears under `path` only once
+ * complete (written to "<path>.tmp", flushed, renamed, directory flushed).
  * Errors: ZERO_EINVAL (bad partition, NULL path/arrays/d_state), ZERO_EIO,
  * ZERO_EDEVICE. */
 zero_status zero_ckpt_save(const char *path, uint64_t psi, uint32_t nd, uint32_t rank,
                            const float *master, const float *exp_avg, const float *exp_avg_sq,
-                           const zero_adam_state_t *d_state, void *stream);
+                           const zero_adam_state_t *d_state, const zero_loss_scale_t *d_scale,
+                           void *stream);
 
 /* Reads and checks the header of a checkpoint file: magic and version, a range
- * equal to zero_partition(psi, nd, rank), and a file size that matches it.
+ * equal to zero_partition(psi, nd, rank), no unknown flag bits, and a file
+ * size that matches them.
  * Errors: ZERO_EINVAL (not a shard, inconsistent range), ZERO_EIO. */
 zero_status zero_ckpt_read_header(const char *path, zero_ckpt_header *out);
 
@@ -381,12 +385,15 @@ zero_status zero_ckpt_read_header(const char *path, zero_ckpt_header *out);
  * step, ranges that tile [0, psi) exactly.  Fills the device arrays master,
  * exp_avg, exp_avg_sq (this rank's n = end - begin elements) from the files
  * that intersect its range and sets *d_state to the saved step with the
- * per-step scalars cleared (the next zero_adam_step recomputes them).
- * Synchronises `stream`.  Errors: ZERO_EINVAL (wrong psi, files from
- * different saves, gaps or overlaps, bad partition), ZERO_EIO, ZERO_EDEVICE. */
+ * per-step scalars cleared (the next zero_adam_step recomputes them).  When
+ * d_scale is not NULL it is set to the saved loss-scale state, which every
+ * file must carry, identically.  Synchronises `stream`.  Errors: ZERO_EINVAL
+ * (wrong psi, files from different saves, gaps or overlaps, bad partition, a
+ * loss-scale state asked for but missing or differing between files),
+ * ZERO_EIO, ZERO_EDEVICE. */
 zero_status zero_ckpt_load(const char *const *paths, uint32_t n_paths, uint64_t psi, uint32_t nd,
                            uint32_t rank, float *master, float *exp_avg, float *exp_avg_sq,
-                           zero_adam_state_t *d_state, void *stream);
+                           zero_adam_state_t *d_state, zero_loss_scale_t *d_scale, void *stream);
 
 #ifdef __cplusplus
 }

@@ -11,13 +11,13 @@ import zero_sharded_mixed_grads_amd as z
 
 
 def write_shard(path, psi, nd, rank, step, master=None, m=None, v=None, magic=b"ZEROCKPT",
-                version=1, extra=b""):
+                version=1, extra=b"", flags=0):
     b, e = oracle.partition(psi, nd, rank)
     n = e - b
     rng = np.random.default_rng(rank)
     arrs = [a if a is not None else rng.standard_normal(n).astype(np.float32)
             for a in (master, m, v)]
-    hdr = struct.pack("<8sIIIIQQQQQ", magic, version, nd, rank, 0, psi, b, e, step, 0)
+    hdr = struct.pack("<8sIIIIQQQQQ", magic, version, nd, rank, 0, psi, b, e, step, flags)
     assert len(hdr) == 64
     with open(path, "wb") as f:
         f.write(hdr)
@@ -77,3 +77,19 @@ def test_load_rejects_incomplete_or_mixed_sets(tmp_path):
     assert _status(z.zero_ckpt_load, paths, *args) == z.ZERO_EINVAL
     assert _status(z.zero_ckpt_load, [], *args) == z.ZERO_EINVAL
     assert _status(z.zero_ckpt_load, paths, psi, 0, 0, *args[3:]) == z.ZERO_EINVAL  # nd = 0
+
+
+def test_loss_scale_record_flag(tmp_path):
+    """Flags bit 0 announces a 32-byte loss-scale record after the arrays: the
+    file size must include it, and unknown flag bits are rejected."""
+    rec = struct.pack("<ddQQ", 1024.0, 1 / 1024.0, 3, 1)
+    p = str(tmp_path / "s.zck")
+    write_shard(p, 10_000, 2, 0, 7, flags=1, extra=rec)
+    h = z.zero_ckpt_read_header(p)
+    assert h.flags == 1 and h.step == 7
+    write_shard(p, 10_000, 2, 0, 7, flags=1)  # record missing
+    assert _status(z.zero_ckpt_read_header, p) == z.ZERO_EIO
+    write_shard(p, 10_000, 2, 0, 7, flags=0, extra=rec)  # record not announced
+    assert _status(z.zero_ckpt_read_header, p) == z.ZERO_EIO
+    write_shard(p, 10_000, 2, 0, 7, flags=2, extra=rec)
+    assert _status(z.zero_ckpt_read_header, p) == z.ZERO_EINVAL

@@ -152,3 +152,75 @@ def test_ckpt_save_errors(tmp_path):
         z.zero_ckpt_save(str(target), n, 1, 0, *bufs, st)
     assert e.value.status == z.ZERO_EIO
     assert target.is_dir() and not (tmp_path / "taken.tmp").exists()
+
+
+def _dyn_steps(bufs, p, grads, st, d_scale, cfg, overflow_at=()):
+    """Steps with dynamic loss scaling on one shard: statistics and AdamW read
+    the scale from the device; the scale is advanced after each step."""
+    n = bufs[0].numel()
+    stats, ws = z.new_grad_stats(dev()), z.new_workspace(n, dev())
+    hp = z.adamw(max_grad_norm=1.0, inv_loss_scale=float("nan"))
+    for k, g in enumerate(grads):
+        if k in overflow_at:
+            g = g.clone()
+            g[n // 2] = 0x7C00  # +inf
+        z.zero_grad_stats(g, "f16", n, float("nan"), ws, ws.numel(), stats, d_scale=d_scale)
+        z.zero_adam_step(hp, g, "f16", *bufs, p, "f16", n, stats, st, d_scale=d_scale)
+        z.zero_loss_scale_update(cfg, stats, d_scale)
+    torch.cuda.synchronize()
+
+
+def test_ckpt_resume_with_dynamic_loss_scale_is_bit_exact(tmp_path):
+    """Two ranks save state and the (identical) loss-scale state; one rank
+    resumes from both files and continues exactly like the run that never
+    stopped, loss scale included.  A load that asks for the loss scale from
+    files without it, or with differing ones, is refused."""
+    n = 300_007
+    cfg = z.loss_scaler(init_scale=2.0 ** 12, growth_interval=2, min_scale=1.0)
+    rng = np.random.default_rng(2)
+    grads = [torch.from_numpy(gen.f32_to_bits16((rng.standard_normal(n) * 3).astype(np.float32),
+                                                "f16").view(np.int16)).to(dev()) for _ in range(6)]
+    th0 = rng.standard_normal(n).astype(np.float32) * 0.02
+    bufs = [torch.from_numpy(th0.copy()).to(dev()), torch.zeros(n, device=dev()),
+            torch.zeros(n, device=dev())]
+    p = torch.zeros(n, dtype=torch.int16, device=dev())
+    st, sc = z.new_adam_state(dev()), z.new_loss_scale(dev())
+    z.zero_loss_scale_init(cfg, sc)
+    _dyn_steps(bufs, p, grads[:3], st, sc, cfg, overflow_at=(1,))
+    paths = []
+    for r in range(2):
+        b, e = oracle.partition(n, 2, r)
+        paths.append(str(tmp_path / f"dyn_r{r}.zck"))
+        z.zero_ckpt_save(paths[-1], n, 2, r, *[x[b:e] for x in bufs], st, d_scale=sc)
+    saved_scale = z.read_loss_scale(sc)
+    saved_step = z.read_adam_state(st).step
+    assert saved_scale.overflows == 1 and saved_step == 2
+    _dyn_steps(bufs, p, grads[3:], st, sc, cfg)
+    # resume as one rank from the two shards
+    bufs2 = _state_bufs(n)
+    p2 = torch.zeros(n, dtype=torch.int16, device=dev())
+    st2, sc2 = z.new_adam_state(dev()), z.new_loss_scale(dev())
+    z.zero_ckpt_load(paths, n, 1, 0, *bufs2, st2, d_scale=sc2)
+    got = z.read_loss_scale(sc2)
+    assert bytes(got) == bytes(saved_scale)
+    _dyn_steps(bufs2, p2, grads[3:], st2, sc2, cfg)
+    for a, b in zip(bufs, bufs2):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert torch.equal(p, p2)
+    assert bytes(z.read_loss_scale(sc)) == bytes(z.read_loss_scale(sc2))
+    assert z.read_adam_state(st2).step == z.read_adam_state(st).step
+    # refusals: no record in one file; records that differ between files (the
+    # re-saved shard keeps the save's step, so only the record differs)
+    b, e = oracle.partition(n, 2, 1)
+    st_saved = z.new_adam_state(dev())
+    st_saved.copy_(torch.from_numpy(
+        np.frombuffer(bytes(z.AdamState(step=saved_step)), np.uint8).copy()))
+    z.zero_ckpt_save(paths[1], n, 2, 1, *[x[b:e] for x in bufs2], st_saved)  # no d_scale
+    with pytest.raises(z.ZeroError) as ex:
+        z.zero_ckpt_load(paths, n, 1, 0, *bufs2, st2, d_scale=sc2)
+    assert ex.value.status == z.ZERO_EINVAL and "no loss-scale" in str(ex.value)
+    z.zero_ckpt_load(paths, n, 1, 0, *bufs2, st2)  # without asking for it: fine
+    z.zero_ckpt_save(paths[1], n, 2, 1, *[x[b:e] for x in bufs2], st_saved, d_scale=sc2)
+    with pytest.raises(z.ZeroError) as ex:
+        z.zero_ckpt_load(paths, n, 1, 0, *bufs2, st2, d_scale=sc2)
+    assert ex.value.status == z.ZERO_EINVAL and "different loss-scale" in str(ex.value)

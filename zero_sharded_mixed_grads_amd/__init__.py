@@ -67,7 +67,7 @@ class LossScale(ctypes.Structure):  # zero_loss_scale_t, device resident
 class CkptHeader(ctypes.Structure):  # zero_ckpt_header
     _fields_ = [("magic", ctypes.c_char * 8), ("version", U32), ("nd", U32), ("rank", U32),
                 ("pad", U32), ("psi", U64), ("begin", U64), ("end", U64), ("step", U64),
-                ("reserved", U64)]
+                ("flags", U64)]
 
 
 assert ctypes.sizeof(GradStats) == 16 and ctypes.sizeof(AdamState) == 64
@@ -119,10 +119,10 @@ def lib():
         L.zero_offload_adam_step.argtypes = [ctypes.POINTER(AdamW), VP, ctypes.c_int, VP, VP,
                                              VP, VP, ctypes.c_int, U64, VP, VP, VP, VP,
                                              ctypes.c_size_t, VP]
-        L.zero_ckpt_save.argtypes = [ctypes.c_char_p, U64, U32, U32, VP, VP, VP, VP, VP]
+        L.zero_ckpt_save.argtypes = [ctypes.c_char_p, U64, U32, U32, VP, VP, VP, VP, VP, VP]
         L.zero_ckpt_read_header.argtypes = [ctypes.c_char_p, ctypes.POINTER(CkptHeader)]
         L.zero_ckpt_load.argtypes = [ctypes.POINTER(ctypes.c_char_p), U32, U64, U32, U32, VP, VP,
-                                     VP, VP, VP]
+                                     VP, VP, VP, VP]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -284,9 +284,10 @@ def zero_offload_adam_step(hp: AdamW, grad, gdtype, master_host, exp_avg_host, e
 
 # ---------------------------------------------------- sharded checkpoints
 def zero_ckpt_save(path: str, psi: int, nd: int, rank: int, master, exp_avg, exp_avg_sq,
-                   d_state, stream=None) -> None:
+                   d_state, stream=None, d_scale=None) -> None:
     _check(lib().zero_ckpt_save(os.fsencode(path), psi, nd, rank, _ptr(master), _ptr(exp_avg),
-                                _ptr(exp_avg_sq), _ptr(d_state), _stream(stream)))
+                                _ptr(exp_avg_sq), _ptr(d_state), _ptr(d_scale),
+                                _stream(stream)))
 
 
 def zero_ckpt_read_header(path: str) -> CkptHeader:
@@ -296,10 +297,11 @@ def zero_ckpt_read_header(path: str) -> CkptHeader:
 
 
 def zero_ckpt_load(paths: Sequence[str], psi: int, nd: int, rank: int, master, exp_avg,
-                   exp_avg_sq, d_state, stream=None) -> None:
+                   exp_avg_sq, d_state, stream=None, d_scale=None) -> None:
     arr = (ctypes.c_char_p * len(paths))(*[os.fsencode(p) for p in paths])
     _check(lib().zero_ckpt_load(arr, len(paths), psi, nd, rank, _ptr(master), _ptr(exp_avg),
-                                _ptr(exp_avg_sq), _ptr(d_state), _stream(stream)))
+                                _ptr(exp_avg_sq), _ptr(d_state), _ptr(d_scale),
+                                _stream(stream)))
 
 
 # ----------------------------------------------- device struct conveniences

@@ -3,7 +3,8 @@
 // it owns; resuming may need a different number of GPUs).
 //
 // File layout (little-endian): a 64-byte zero_ckpt_header, then the rank's
-// fp32 master, momentum and variance, n = end - begin elements each.  Save
+// fp32 master, momentum and variance, n = end - begin elements each, then,
+// when the header's flags bit 0 is set, the 32-byte loss-scale state.  Save
 // writes to "<path>.tmp", flushes it to storage and renames it over <path>,
 // so a crash never leaves a half-written file under the final name.  Load
 // takes the shard files of a saved run with any number of ranks, checks that
@@ -32,6 +33,15 @@ namespace {
 constexpr char kMagic[8] = {'Z', 'E', 'R', 'O', 'C', 'K', 'P', 'T'};
 constexpr uint32_t kVersion = 1;
 constexpr uint64_t kChunk = 64ull << 20;  // bytes staged through host memory at a time
+constexpr uint64_t kFlagLossScale = 1;    // a zero_loss_scale_t follows the arrays
+
+static_assert(sizeof(zero_loss_scale_t) == 32, "loss-scale record is 32 bytes");
+
+uint64_t file_bytes(const zero_ckpt_header &h)
+{
+    return sizeof h + 12 * (h.end - h.begin) +
+           ((h.flags & kFlagLossScale) ? sizeof(zero_loss_scale_t) : 0);
+}
 
 static_assert(sizeof(zero_ckpt_header) == 64, "checkpoint header is 64 bytes");
 
@@ -102,7 +112,7 @@ zero_status hip_check(hipError_t e, const char *what)
 extern "C" zero_status zero_ckpt_save(const char *path, uint64_t psi, uint32_t nd, uint32_t rank,
                                       const float *master, const float *exp_avg,
                                       const float *exp_avg_sq, const zero_adam_state_t *d_state,
-                                      void *stream)
+                                      const zero_loss_scale_t *d_scale, void *stream)
 {
     if (!path || !d_state)
         return fail(ZERO_EINVAL, "zero_ckpt_save: NULL path or d_state");
@@ -115,8 +125,12 @@ extern "C" zero_status zero_ckpt_save(const char *path, uint64_t psi, uint32_t n
         return fail(ZERO_EINVAL, "zero_ckpt_save: NULL state array with n > 0");
     hipStream_t s = (hipStream_t)stream;
     zero_adam_state_t state;
+    zero_loss_scale_t scale{};
     if ((st = hip_check(hipMemcpyAsync(&state, d_state, sizeof state, hipMemcpyDeviceToHost, s),
                         "zero_ckpt_save: reading the step state")) != ZERO_OK ||
+        (d_scale &&
+         (st = hip_check(hipMemcpyAsync(&scale, d_scale, sizeof scale, hipMemcpyDeviceToHost, s),
+                         "zero_ckpt_save: reading the loss-scale state")) != ZERO_OK) ||
         (st = hip_check(hipStreamSynchronize(s), "zero_ckpt_save: stream")) != ZERO_OK)
         return st;
 
@@ -129,6 +143,7 @@ extern "C" zero_status zero_ckpt_save(const char *path, uint64_t psi, uint32_t n
     h.begin = begin;
     h.end = end;
     h.step = state.step;
+    h.flags = d_scale ? kFlagLossScale : 0;
 
     const std::string tmp = std::string(path) + ".tmp";
     Fd f;
@@ -152,6 +167,8 @@ extern "C" zero_status zero_ckpt_save(const char *path, uint64_t psi, uint32_t n
                             strerror(errno));
         }
     }
+    if (d_scale && !write_all(f.fd, &scale, sizeof scale))
+        return fail(ZERO_EIO, "zero_ckpt_save: writing %s: %s", tmp.c_str(), strerror(errno));
     if (fsync(f.fd) != 0)
         return fail(ZERO_EIO, "zero_ckpt_save: fsync %s: %s", tmp.c_str(), strerror(errno));
     const int fd = f.fd;
@@ -181,13 +198,15 @@ extern "C" zero_status zero_ckpt_read_header(const char *path, zero_ckpt_header 
     if (std::memcmp(h.magic, kMagic, sizeof kMagic) != 0 || h.version != kVersion)
         return fail(ZERO_EINVAL, "zero_ckpt_read_header: %s is not a version-%u shard", path,
                     kVersion);
+    if (h.flags & ~kFlagLossScale)
+        return fail(ZERO_EINVAL, "zero_ckpt_read_header: %s has unknown flags %llx", path,
+                    (unsigned long long)h.flags);
     uint64_t b, e;
     if (zero_partition(h.psi, h.nd, h.rank, &b, &e) != ZERO_OK || b != h.begin || e != h.end)
         return fail(ZERO_EINVAL, "zero_ckpt_read_header: %s: range [%llu, %llu) is not rank %u of %u",
                     path, (unsigned long long)h.begin, (unsigned long long)h.end, h.rank, h.nd);
     struct stat sb;
-    if (fstat(f.fd, &sb) != 0 ||
-        (uint64_t)sb.st_size != sizeof h + 12 * (h.end - h.begin))
+    if (fstat(f.fd, &sb) != 0 || (uint64_t)sb.st_size != file_bytes(h))
         return fail(ZERO_EIO, "zero_ckpt_read_header: %s has the wrong size", path);
     *out = h;
     return ZERO_OK;
@@ -195,7 +214,8 @@ extern "C" zero_status zero_ckpt_read_header(const char *path, zero_ckpt_header 
 
 extern "C" zero_status zero_ckpt_load(const char *const *paths, uint32_t n_paths, uint64_t psi,
                                       uint32_t nd, uint32_t rank, float *master, float *exp_avg,
-                                      float *exp_avg_sq, zero_adam_state_t *d_state, void *stream)
+                                      float *exp_avg_sq, zero_adam_state_t *d_state,
+                                      zero_loss_scale_t *d_scale, void *stream)
 {
     if (!paths || n_paths == 0 || !d_state)
         return fail(ZERO_EINVAL, "zero_ckpt_load: no shard files or NULL d_state");
@@ -238,6 +258,28 @@ extern "C" zero_status zero_ckpt_load(const char *const *paths, uint32_t n_paths
         return fail(ZERO_EINVAL, "zero_ckpt_load: %u shard files do not cover all %u ranks",
                     n_paths, hs[0].nd);
 
+    // the loss-scale record, when asked for: present and identical in every file
+    zero_loss_scale_t scale{};
+    if (d_scale) {
+        for (uint32_t i = 0; i < n_paths; ++i) {
+            if (!(hs[i].flags & kFlagLossScale))
+                return fail(ZERO_EINVAL, "zero_ckpt_load: %s holds no loss-scale state",
+                            paths[i]);
+            Fd f;
+            f.fd = open(paths[i], O_RDONLY);
+            zero_loss_scale_t r;
+            if (f.fd < 0 ||
+                !read_at(f.fd, &r, sizeof r, file_bytes(hs[i]) - sizeof r))
+                return fail(ZERO_EIO, "zero_ckpt_load: reading the loss-scale state of %s",
+                            paths[i]);
+            if (i == 0)
+                scale = r;
+            else if (std::memcmp(&r, &scale, sizeof r) != 0)
+                return fail(ZERO_EINVAL, "zero_ckpt_load: %s has a different loss-scale state",
+                            paths[i]);
+        }
+    }
+
     hipStream_t s = (hipStream_t)stream;
     if ((st = hip_check(hipStreamSynchronize(s), "zero_ckpt_load: stream")) != ZERO_OK)
         return st;
@@ -272,6 +314,10 @@ extern "C" zero_status zero_ckpt_load(const char *const *paths, uint32_t n_paths
     state.step = hs[0].step;
     if ((st = hip_check(hipMemcpyAsync(d_state, &state, sizeof state, hipMemcpyHostToDevice, s),
                         "zero_ckpt_load: writing the step state")) != ZERO_OK)
+        return st;
+    if (d_scale &&
+        (st = hip_check(hipMemcpyAsync(d_scale, &scale, sizeof scale, hipMemcpyHostToDevice, s),
+                        "zero_ckpt_load: writing the loss-scale state")) != ZERO_OK)
         return st;
     return hip_check(hipStreamSynchronize(s), "zero_ckpt_load: stream");
 }
