@@ -263,7 +263,11 @@ __device__ __forceinline__ double wave_sum(double x)
 }
 
 // ================================================================ flatten
-constexpr int kMaxSegs = 96;         // segments per launch (kernel-argument table)
+// Segments per launch (kernel-argument table), found by a two-level search:
+// 16 coarse entries, then 8 fine ones, each level one scalar load.
+constexpr int kSegFan = 8;
+constexpr int kSegCoarse = 16;
+constexpr int kMaxSegs = kSegCoarse * kSegFan;
 constexpr int kFlatChunksPerThread = ZERO_FLAT_CPT;
 constexpr uint64_t kFlatTileChunks = (uint64_t)kBlock * kFlatChunksPerThread;
 
@@ -271,16 +275,33 @@ constexpr uint64_t kFlatTileChunks = (uint64_t)kBlock * kFlatChunksPerThread;
 // 16-bit values each tile writes (fp16 or bf16), one fp64 partial per tile.
 enum { kCopy = 0, kStatsF16 = 1, kStatsBF16 = 2 };
 
+constexpr uint32_t kTilePad = 0x7fffffffu;  // table entries past the last segment
+
 struct FlatArgs {
+    uint32_t coarse[kSegCoarse];   // coarse[j] = tile_lo[kSegFan * j] (one 64-byte load)
     char *dst;                     // element 0 of the destination range
     double *part;                  // per-tile partial sums (stats modes)
     uint64_t tile_base;            // global index of this launch's first tile
     uint32_t n_segs;
     uint32_t dst_phase;            // (dst address mod 16) / element size
+    uint32_t n_tiles;              // tiles of this launch
+    uint32_t tile_lo[kMaxSegs + kSegFan];  // first tile of each segment, then
+                                           // n_tiles, then kTilePad
     uint64_t seg_lo[kMaxSegs + 1]; // destination element offset of each segment
-    uint64_t tile_lo[kMaxSegs + 1];// first tile of each segment; last = total
     const char *src[kMaxSegs];     // address of each segment's first source element
 };
+
+// Entries c of a table that are <= t, for values below 2^31: t - c is then
+// negative exactly when c > t.
+template <int N>
+__device__ __forceinline__ uint32_t count_le(const uint32_t *c, uint32_t t)
+{
+    uint32_t above = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        above += (t - c[i]) >> 31;
+    return N - above;
+}
 
 template <bool BF16>
 __device__ __forceinline__ void accum2(uint32_t w, double &acc)
@@ -349,75 +370,72 @@ template <int ES, int MODE>
 __global__ void __launch_bounds__(kBlock) flatten_segments(FlatArgs a)
 {
     constexpr uint64_t V = 16 / ES;  // elements per 16-byte line
-    const uint64_t total_tiles = a.tile_lo[a.n_segs];
-    for (uint64_t tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
-        // segment of this tile: largest s with tile_lo[s] <= tile (uniform)
-        uint32_t lo = 0, hi = a.n_segs;
-        while (hi - lo > 1) {
-            const uint32_t mid = (lo + hi) / 2;
-            if (a.tile_lo[mid] <= tile) lo = mid; else hi = mid;
-        }
-        const uint32_t s = lo;
-        const uint64_t e_lo = a.seg_lo[s], e_hi = a.seg_lo[s + 1];
-        const uint64_t ph = a.dst_phase;
-        // full destination lines inside the segment: [c0, c1) in line units
-        const uint64_t c0 = (e_lo + ph + V - 1) / V, c1 = (e_hi + ph) / V;
-        const bool has_full = c1 > c0;
-        const uint64_t k = tile - a.tile_lo[s];
-        const char *src = a.src[s];
-        double acc = 0.0;
-        if (k == 0) {
-            // partial lines at both ends, element by element
-            const uint64_t head_end = has_full ? c0 * V - ph : e_hi;
-            const uint64_t tail_beg = has_full ? c1 * V - ph : e_hi;
-            const uint64_t n_head = head_end - e_lo, n_tail = e_hi - tail_beg;
-            const uint64_t i = threadIdx.x;
-            if (i < n_head + n_tail) {
-                const uint64_t e = i < n_head ? e_lo + i : tail_beg + (i - n_head);
-                if constexpr (ES == 2) {
-                    const uint16_t v = reinterpret_cast<const uint16_t *>(src)[e - e_lo];
-                    reinterpret_cast<uint16_t *>(a.dst)[e] = v;
-                    if constexpr (MODE != kCopy) {
-                        const double x = (double)to_f32<MODE == kStatsBF16>(v);
-                        acc = fma(x, x, acc);
-                    }
-                } else {
-                    reinterpret_cast<uint32_t *>(a.dst)[e] =
-                        reinterpret_cast<const uint32_t *>(src)[e - e_lo];
+    const uint32_t tile = blockIdx.x;  // one tile per block: the grid is the tile count
+    // segment of this tile: the largest s with tile_lo[s] <= tile (uniform).
+    // tile_lo rises strictly from tile_lo[0] = 0 and then reads values above
+    // every tile, so s + 1 is the count of entries <= tile: found as a count
+    // among the coarse entries, then among the chosen slot's fine entries.
+    const uint32_t j = count_le<kSegCoarse>(a.coarse, tile) - 1;
+    const uint32_t s = j * kSegFan + count_le<kSegFan>(a.tile_lo + j * kSegFan, tile) - 1;
+    const uint64_t e_lo = a.seg_lo[s], e_hi = a.seg_lo[s + 1];
+    const uint64_t ph = a.dst_phase;
+    // full destination lines inside the segment: [c0, c1) in line units
+    const uint64_t c0 = (e_lo + ph + V - 1) / V, c1 = (e_hi + ph) / V;
+    const bool has_full = c1 > c0;
+    const uint64_t k = tile - a.tile_lo[s];  // tile within the segment
+    const char *src = a.src[s];
+    double acc = 0.0;
+    if (k == 0) {
+        // partial lines at both ends, element by element
+        const uint64_t head_end = has_full ? c0 * V - ph : e_hi;
+        const uint64_t tail_beg = has_full ? c1 * V - ph : e_hi;
+        const uint64_t n_head = head_end - e_lo, n_tail = e_hi - tail_beg;
+        const uint64_t i = threadIdx.x;
+        if (i < n_head + n_tail) {
+            const uint64_t e = i < n_head ? e_lo + i : tail_beg + (i - n_head);
+            if constexpr (ES == 2) {
+                const uint16_t v = reinterpret_cast<const uint16_t *>(src)[e - e_lo];
+                reinterpret_cast<uint16_t *>(a.dst)[e] = v;
+                if constexpr (MODE != kCopy) {
+                    const double x = (double)to_f32<MODE == kStatsBF16>(v);
+                    acc = fma(x, x, acc);
                 }
+            } else {
+                reinterpret_cast<uint32_t *>(a.dst)[e] =
+                    reinterpret_cast<const uint32_t *>(src)[e - e_lo];
             }
         }
-        if (has_full) {
-            const uint64_t t_beg = k * kFlatTileChunks;
-            const uint64_t t_end =
-                (t_beg + kFlatTileChunks < c1 - c0) ? t_beg + kFlatTileChunks : c1 - c0;
-            // first full line's source bytes and their 16-byte phase (uniform)
-            const uintptr_t s0 = (uintptr_t)(src + (c0 * V - ph - e_lo) * ES);
-            const uint32_t sb = (uint32_t)(s0 & 15u);
-            const char *sl = (const char *)(s0 - sb);
-            char *dl = a.dst + (c0 * V - ph) * ES;
-            switch (sb) {
-            case 0: flatten_full_chunks<ES, 0, MODE>(sl, dl, t_beg, t_end, acc); break;
-            case 4: flatten_full_chunks<ES, 4, MODE>(sl, dl, t_beg, t_end, acc); break;
-            case 8: flatten_full_chunks<ES, 8, MODE>(sl, dl, t_beg, t_end, acc); break;
-            case 12: flatten_full_chunks<ES, 12, MODE>(sl, dl, t_beg, t_end, acc); break;
-            default:
-                if constexpr (ES == 2) {
-                    switch (sb) {
-                    case 2: flatten_full_chunks<ES, 2, MODE>(sl, dl, t_beg, t_end, acc); break;
-                    case 6: flatten_full_chunks<ES, 6, MODE>(sl, dl, t_beg, t_end, acc); break;
-                    case 10: flatten_full_chunks<ES, 10, MODE>(sl, dl, t_beg, t_end, acc); break;
-                    default: flatten_full_chunks<ES, 14, MODE>(sl, dl, t_beg, t_end, acc); break;
-                    }
+    }
+    if (has_full) {
+        const uint64_t t_beg = k * kFlatTileChunks;
+        const uint64_t t_end =
+            (t_beg + kFlatTileChunks < c1 - c0) ? t_beg + kFlatTileChunks : c1 - c0;
+        // first full line's source bytes and their 16-byte phase (uniform)
+        const uintptr_t s0 = (uintptr_t)(src + (c0 * V - ph - e_lo) * ES);
+        const uint32_t sb = (uint32_t)(s0 & 15u);
+        const char *sl = (const char *)(s0 - sb);
+        char *dl = a.dst + (c0 * V - ph) * ES;
+        switch (sb) {
+        case 0: flatten_full_chunks<ES, 0, MODE>(sl, dl, t_beg, t_end, acc); break;
+        case 4: flatten_full_chunks<ES, 4, MODE>(sl, dl, t_beg, t_end, acc); break;
+        case 8: flatten_full_chunks<ES, 8, MODE>(sl, dl, t_beg, t_end, acc); break;
+        case 12: flatten_full_chunks<ES, 12, MODE>(sl, dl, t_beg, t_end, acc); break;
+        default:
+            if constexpr (ES == 2) {
+                switch (sb) {
+                case 2: flatten_full_chunks<ES, 2, MODE>(sl, dl, t_beg, t_end, acc); break;
+                case 6: flatten_full_chunks<ES, 6, MODE>(sl, dl, t_beg, t_end, acc); break;
+                case 10: flatten_full_chunks<ES, 10, MODE>(sl, dl, t_beg, t_end, acc); break;
+                default: flatten_full_chunks<ES, 14, MODE>(sl, dl, t_beg, t_end, acc); break;
                 }
-                break;
             }
+            break;
         }
-        if constexpr (MODE != kCopy) {
-            const double t = block_sum(acc);
-            if (threadIdx.x == 0)
-                a.part[a.tile_base + tile] = t;
-        }
+    }
+    if constexpr (MODE != kCopy) {
+        const double t = block_sum(acc);
+        if (threadIdx.x == 0)
+            a.part[a.tile_base + tile] = t;
     }
 }
 
@@ -457,11 +475,12 @@ size_t stats_workspace_bytes(uint64_t n) { return partials_bytes(stats_tiles_max
 template <bool BF16>
 __global__ void __launch_bounds__(kBlock)
     stats_pass1(const uint16_t *g, uint64_t head, uint64_t nchunks, uint64_t tail_beg, uint64_t n,
-                double *part)
+                uint64_t tile0, double *part)
 {
     double acc = 0.0;
     const uint4 *lines = reinterpret_cast<const uint4 *>(g + head);
-    const uint64_t base = (uint64_t)blockIdx.x * kStatsTileLines + threadIdx.x;
+    const uint64_t tile = tile0 + blockIdx.x;
+    const uint64_t base = tile * kStatsTileLines + threadIdx.x;
     uint4 w[ZERO_STATS_LINES];
 #pragma unroll
     for (int j = 0; j < ZERO_STATS_LINES; ++j) {
@@ -475,7 +494,7 @@ __global__ void __launch_bounds__(kBlock)
         accum2<BF16>(w[j].z, acc);
         accum2<BF16>(w[j].w, acc);
     }
-    if (blockIdx.x == 0) {  // elements outside the aligned lines: [0, head) and [tail_beg, n)
+    if (tile == 0) {  // elements outside the aligned lines: [0, head) and [tail_beg, n)
         const uint64_t n_edge = head + (n - tail_beg);
         if (threadIdx.x < n_edge) {
             const uint64_t e = threadIdx.x < head ? threadIdx.x : tail_beg + (threadIdx.x - head);
@@ -485,7 +504,7 @@ __global__ void __launch_bounds__(kBlock)
     }
     const double t = block_sum(acc);
     if (threadIdx.x == 0)
-        part[blockIdx.x] = t;
+        part[tile] = t;
 }
 
 // Block b sums partials [b*kReduceGroup, (b+1)*kReduceGroup) in a fixed order.
@@ -785,6 +804,11 @@ uint32_t resident_blocks(K kernel)
     return v;
 }
 
+// Blocks of one launch.  A dispatch is kept below 2^31 work-items, inside
+// both the dispatch packet's 32-bit grid size and the runtime's int-typed grid
+// limits; a multiple of 8, so that a capped grid spans whole rounds of XCDs.
+constexpr uint64_t kMaxLaunchBlocks = 0x7fffffffu / kBlock / 8 * 8;
+
 inline uint32_t grid_for(uint64_t work_items, uint64_t per_block, uint32_t max_blocks)
 {
     uint64_t b = (work_items + per_block - 1) / per_block;
@@ -793,12 +817,15 @@ inline uint32_t grid_for(uint64_t work_items, uint64_t per_block, uint32_t max_b
     return (uint32_t)b;
 }
 
+// Tiles of one gather launch: one block each (and fewer than kTilePad).
+constexpr uint64_t kMaxLaunchTiles = kMaxLaunchBlocks;
+static_assert(kMaxLaunchTiles < kTilePad, "tile indices must stay below the table padding");
+
 template <int ES, int MODE>
 zero_status flatten_launch(FlatArgs &a, hipStream_t stream)
 {
-    // one tile per block; the kernel's tile loop covers a capped grid
-    const uint32_t grid = grid_for(a.tile_lo[a.n_segs], 1, 0x7ffffff0u);
-    hipLaunchKernelGGL((flatten_segments<ES, MODE>), dim3(grid), dim3(kBlock), 0, stream, a);
+    // one tile per block
+    hipLaunchKernelGGL((flatten_segments<ES, MODE>), dim3(a.n_tiles), dim3(kBlock), 0, stream, a);
     return launch_status("zero_bucket_flatten");
 }
 
@@ -850,6 +877,15 @@ zero_status flatten_impl(const char *what, const void *const *tensor_ptrs, const
     if (count > UINT64_MAX / es)
         return fail(ZERO_EINVAL, "%s: count too large", what);
 
+    // tiles of the segment [d_lo, d_hi) of the destination: its full 16-byte
+    // lines in tiles, or one tile for a segment without a full line
+    const uint64_t V = 16 / es, ph = ((uintptr_t)dst & 15u) / es;
+    auto seg_tiles = [&](uint64_t d_lo, uint64_t d_hi) {
+        const uint64_t c0 = (d_lo + ph + V - 1) / V, c1 = (d_hi + ph) / V;
+        const uint64_t full = c1 > c0 ? c1 - c0 : 0;
+        return full ? (full + kFlatTileChunks - 1) / kFlatTileChunks : (uint64_t)1;
+    };
+
     // check every intersecting tensor before launching anything
     uint64_t start = 0;
     for (uint32_t i = 0; i < n_tensors; ++i) {
@@ -874,7 +910,30 @@ zero_status flatten_impl(const char *what, const void *const *tensor_ptrs, const
     FlatArgs a{};
     a.dst = (char *)dst;
     a.part = part;
-    a.dst_phase = (uint32_t)(((uintptr_t)dst & 15u) / es);
+    a.dst_phase = (uint32_t)ph;
+    uint64_t launch_tiles = 0;  // tiles of the segments in the table
+    // launches the segments in the table, after completing the search tables
+    auto launch = [&]() -> zero_status {
+        a.n_tiles = (uint32_t)launch_tiles;
+        a.tile_lo[a.n_segs] = a.n_tiles;
+        for (uint32_t i = a.n_segs + 1; i < (uint32_t)(kMaxSegs + kSegFan); ++i)
+            a.tile_lo[i] = kTilePad;
+        for (int j = 0; j < kSegCoarse; ++j)
+            a.coarse[j] = a.tile_lo[kSegFan * j];
+        zero_status st;
+        if (es == 4)
+            st = flatten_launch<4, kCopy>(a, stream);
+        else if (mode == kStatsF16)
+            st = flatten_launch<2, kStatsF16>(a, stream);
+        else if (mode == kStatsBF16)
+            st = flatten_launch<2, kStatsBF16>(a, stream);
+        else
+            st = flatten_launch<2, kCopy>(a, stream);
+        a.tile_base += launch_tiles;
+        a.n_segs = 0;
+        launch_tiles = 0;
+        return st;
+    };
     start = 0;
     for (uint32_t i = 0; i < n_tensors; ++i) {
         const uint64_t t_lo = start, t_hi = start + numel[i];
@@ -883,34 +942,32 @@ zero_status flatten_impl(const char *what, const void *const *tensor_ptrs, const
         const uint64_t hi = t_hi < range_end ? t_hi : range_end;
         if (lo >= hi)
             continue;
-        const char *src = (const char *)tensor_ptrs[i];
-        // one segment: destination elements [lo - range_begin, hi - range_begin)
-        const uint32_t s = a.n_segs;
-        const uint64_t d_lo = lo - range_begin, d_hi = hi - range_begin;
-        const uint64_t V = 16 / es, ph = a.dst_phase;
-        const uint64_t c0 = (d_lo + ph + V - 1) / V, c1 = (d_hi + ph) / V;
-        const uint64_t full = c1 > c0 ? c1 - c0 : 0;
-        const uint64_t tiles = full ? (full + kFlatTileChunks - 1) / kFlatTileChunks : 1;
-        a.seg_lo[s] = d_lo;
-        a.seg_lo[s + 1] = d_hi;
-        a.src[s] = src + (lo - t_lo) * es;
-        a.tile_lo[s + 1] = a.tile_lo[s] + tiles;
-        a.n_segs = s + 1;
-        if (a.n_segs == kMaxSegs || hi == range_end) {
-            zero_status st;
-            if (es == 4)
-                st = flatten_launch<4, kCopy>(a, stream);
-            else if (mode == kStatsF16)
-                st = flatten_launch<2, kStatsF16>(a, stream);
-            else if (mode == kStatsBF16)
-                st = flatten_launch<2, kStatsBF16>(a, stream);
-            else
-                st = flatten_launch<2, kCopy>(a, stream);
-            if (st != ZERO_OK)
-                return st;
-            a.tile_base += a.tile_lo[a.n_segs];
-            a.n_segs = 0;
-            a.tile_lo[0] = 0;
+        // destination elements [d_lo, d_hi), as one segment, or as several if the
+        // launch has room for fewer tiles: a piece then ends after `room` tiles
+        // of whole lines, so the pieces have the tiles of the whole
+        uint64_t d_lo = lo - range_begin;
+        const uint64_t d_hi = hi - range_begin;
+        const char *src = (const char *)tensor_ptrs[i] + (lo - t_lo) * es;
+        while (d_lo < d_hi) {
+            const uint64_t room = kMaxLaunchTiles - launch_tiles;  // > 0
+            uint64_t tiles = seg_tiles(d_lo, d_hi), d_end = d_hi;
+            if (tiles > room) {
+                d_end = ((d_lo + ph + V - 1) / V + room * kFlatTileChunks) * V - ph;
+                tiles = room;
+            }
+            const uint32_t s = a.n_segs;
+            a.seg_lo[s] = d_lo;
+            a.seg_lo[s + 1] = d_end;
+            a.src[s] = src;
+            a.tile_lo[s] = (uint32_t)launch_tiles;
+            launch_tiles += tiles;
+            a.n_segs = s + 1;
+            src += (d_end - d_lo) * es;
+            d_lo = d_end;
+            if (a.n_segs == kMaxSegs || launch_tiles == kMaxLaunchTiles ||
+                (d_lo == d_hi && hi == range_end))
+                if (zero_status st = launch(); st != ZERO_OK)
+                    return st;
         }
     }
     *n_tiles = a.tile_base;
@@ -1010,20 +1067,23 @@ extern "C" zero_status zero_grad_stats(const void *grad, zero_dtype gdt, uint64_
     const uint64_t nchunks = (n - head) / 8;
     const uint64_t tail_beg = head + 8 * nchunks;
     uint64_t tiles = (nchunks + kStatsTileLines - 1) / kStatsTileLines;
-    if (tiles == 0) tiles = 1;  // block 0 also takes the elements outside the lines
-    if (tiles > 0x7fffffffu)
-        return fail(ZERO_EINVAL, "zero_grad_stats: n too large for one call");
+    if (tiles == 0) tiles = 1;  // tile 0 also takes the elements outside the lines
     double *part = (double *)workspace;
     const uint16_t *g = (const uint16_t *)grad;
-    if (gdt == ZERO_BF16)
-        hipLaunchKernelGGL(stats_pass1<true>, dim3((uint32_t)tiles), dim3(kBlock), 0, s, g, head,
-                           nchunks, tail_beg, n, part);
-    else
-        hipLaunchKernelGGL(stats_pass1<false>, dim3((uint32_t)tiles), dim3(kBlock), 0, s, g, head,
-                           nchunks, tail_beg, n, part);
-    const zero_status st = launch_status("zero_grad_stats pass 1");
-    if (st != ZERO_OK)
-        return st;
+    // one tile per block, in launches of at most kMaxLaunchBlocks blocks
+    for (uint64_t t0 = 0; t0 < tiles; t0 += kMaxLaunchBlocks) {
+        const uint32_t grid = (uint32_t)(tiles - t0 < kMaxLaunchBlocks ? tiles - t0
+                                                                       : kMaxLaunchBlocks);
+        if (gdt == ZERO_BF16)
+            hipLaunchKernelGGL(stats_pass1<true>, dim3(grid), dim3(kBlock), 0, s, g, head,
+                               nchunks, tail_beg, n, t0, part);
+        else
+            hipLaunchKernelGGL(stats_pass1<false>, dim3(grid), dim3(kBlock), 0, s, g, head,
+                               nchunks, tail_beg, n, t0, part);
+        const zero_status st = launch_status("zero_grad_stats pass 1");
+        if (st != ZERO_OK)
+            return st;
+    }
     return reduce_partials(part, tiles, inv_loss_scale, d_scale, d_stats, s);
 }
 
@@ -1096,7 +1156,7 @@ void launch_adam_variant(const AdamArgs &a, uint64_t work, hipStream_t s)
     auto kernel = adamw_stream<GB, PB, GA, PA>;
     const uint64_t per_block = (uint64_t)kBlock * kAdamUnroll;
     // one tile per block; the element-wise fallback keeps a resident grid
-    uint32_t grid = a.nchunks ? grid_for(a.nchunks, per_block, 0x7ffffff0u)
+    uint32_t grid = a.nchunks ? grid_for(a.nchunks, per_block, kMaxLaunchBlocks)
                               : grid_for(work, per_block, resident_blocks(kernel));
     if (a.nchunks)
         grid = (grid + 7) / 8 * 8;  // whole rounds of the 8 XCDs; spare blocks find no tile
