@@ -357,6 +357,31 @@ def ckpt_bench(cfg_idx: int = 5, reps: int = 2):
                                "round_trip_bit_exact": same}}), flush=True)
 
 
+def host_stream_ceiling(reps: int = 5):
+    """Host memory bandwidth with torch's intra-op threads on 4 GiB fp32 arrays,
+    well beyond the host caches: an in-place scale (each element read and
+    written back, as the offloaded update does to master, m and v) and an
+    out-of-place copy (counted as 8 B per element, though its stores first
+    read their lines for ownership).  Returns the best of `reps` passes of
+    each, in GB/s."""
+    import torch
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.float32)
+    b = torch.empty_like(a)
+    out = {"threads": torch.get_num_threads()}
+    for name, fn in (("copy", lambda: torch.mul(a, 1.0, out=b)), ("in_place", lambda: a.mul_(1.0))):
+        fn()
+        best = min(_host_time(fn) for _ in range(reps))
+        out[f"{name}_GB/s"] = 2 * 4 * n / best / 1e9
+    return out
+
+
+def _host_time(fn):
+    t0 = time.perf_counter()
+    fn()
+    return time.perf_counter() - t0
+
+
 def offload_bench(cfg_idx: int, steps: int, warmup: int, chunk: int = 1 << 24):
     """The optimizer step with master/m/v in host memory (zero_offload_adam_step)
     on the same shard: gradients and params on the device, statistics on the
@@ -404,11 +429,19 @@ def offload_bench(cfg_idx: int, steps: int, warmup: int, chunk: int = 1 << 24):
     cpu = next((l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
                 if l.startswith("model name")), "unknown")
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    del master, m, v
+    log("[bench] host memory ceiling")
+    ceiling = host_stream_ceiling()
+    # host DRAM bytes per param: master, m, v read and written (24), the staged
+    # gradient written by DMA and read (4), the staged param written and read by DMA (4)
+    host_gbs = 32 * n / (ms * 1e-3) / 1e9
     print(json.dumps({"offload": {
         "workload": cfg.name + f"-nd{cfg.nd}-rank{cfg.rank}", "shard_params": n,
         "steps": steps, "warmup": warmup, "ms_per_step": ms, "params_per_s": n / (ms * 1e-3),
         "pcie_GB/s": 4 * n / (ms * 1e-3) / 1e9,
         "host_state_GB/s": 24 * n / (ms * 1e-3) / 1e9,
+        "host_dram_GB/s": host_gbs, "host_ceiling": ceiling,
+        "frac_of_host_in_place": host_gbs / ceiling["in_place_GB/s"],
         "chunk_elems": chunk, "host_threads": threads, "host_cpu": cpu}}), flush=True)
 
 
