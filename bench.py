@@ -133,23 +133,23 @@ class Workload:
         log(f"[bench] inputs resident in HBM after {time.time() - t0:.1f}s "
             f"({torch.cuda.memory_allocated() / 1e9:.1f} GB allocated)")
 
-    def step(self, ev=None, fused=True):
-        """One pass of the hot path; ev: optional list of 4 events recorded
-        around gather / stats / adam on the launch stream.  fused: gather the
-        rank's gradients and compute their statistics in one pass (the rank's
-        per-tensor gradients are final at Nd = 1); otherwise gather one fused
-        buffer at a time, then a separate statistics pass."""
+    def step(self, marks=None, fused=True):
+        """One pass of the hot path.  fused: gather the rank's gradients and
+        compute their statistics in one pass (the rank's per-tensor gradients
+        are final at Nd = 1); otherwise gather one fused buffer at a time, then
+        a separate statistics pass.  marks: optional events recorded on the
+        launch stream between the phases: after the gather and statistics
+        (fused, one event), or after the gather and after the statistics
+        (unfused, two events)."""
         z, cfg = self.z, self.cfg
         stream = self.torch.cuda.current_stream()
         s = stream.cuda_stream
         b, e = z.zero_partition(cfg.psi, cfg.nd, cfg.rank)
         B = cfg.bucket_elems or cfg.psi
-        if ev: ev[0].record(stream)
         if fused:
             z.zero_bucket_flatten_stats(self.ptrs, cfg.numels, cfg.dtype, b, e - b, self.g,
                                         cfg.hp.inv_loss_scale, self.fws, self.fws.numel(),
                                         self.stats, s)
-            if ev: ev[1].record(stream)
         else:
             lo = b
             while lo < e:  # one fused buffer at a time, this rank's part of it
@@ -157,13 +157,12 @@ class Workload:
                 z.zero_bucket_flatten(self.ptrs, cfg.numels, cfg.dtype, lo, hi - lo,
                                       self.g.data_ptr() + 2 * (lo - b), s)
                 lo = hi
-            if ev: ev[1].record(stream)
+            if marks: marks[0].record(stream)
             z.zero_grad_stats(self.g, cfg.dtype, self.n, cfg.hp.inv_loss_scale, self.ws,
                               self.ws.numel(), self.stats, s)
-        if ev: ev[2].record(stream)
+        if marks: marks[-1].record(stream)
         z.zero_adam_step(self.hp, self.g, cfg.dtype, self.master, self.m, self.v, self.p,
                          cfg.dtype, self.n, self.stats, self.state, s)
-        if ev: ev[3].record(stream)
 
 
 def cpu_baseline(w, target_s: float = 12.0):
@@ -448,8 +447,8 @@ def offload_bench(cfg_idx: int, steps: int, warmup: int, chunk: int = 1 << 24):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -495,14 +494,25 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done")
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # HIP events on the launch stream: one at each step boundary (shared by
+    # consecutive steps) and one (fused) or two (unfused) between the phases
+    def event():
+        return torch.cuda.Event(enable_timing=True)
+    bounds = [event() for _ in range(args.steps + 1)]
+    marks = [[event() for _ in range(1 if fused else 2)] for _ in range(args.steps)]
+    stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    bounds[0].record(stream)
     for k in range(args.steps):
-        w.step(evs[k], fused=fused)
+        w.step(marks[k], fused=fused)
+        bounds[k + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = np.array([[a.elapsed_time(b) for a, b in zip(e[:-1], e[1:])] for e in evs])
+    # per step: gather (+ stats when fused), stats (unfused), adam
+    ms = np.array([[bounds[k].elapsed_time(marks[k][0]),
+                    marks[k][0].elapsed_time(marks[k][-1]),
+                    marks[k][-1].elapsed_time(bounds[k + 1])] for k in range(args.steps)])
     flat_ms, stats_ms, adam_ms = ms.mean(axis=0)
     log(f"[bench] timed {args.steps} steps in {wall:.3f}s ({'fused' if fused else 'unfused'}); "
         f"per step gather {flat_ms:.3f} ms, stats {stats_ms:.3f} ms, adam {adam_ms:.3f} ms "
