@@ -23,7 +23,9 @@
  *    the workspace size of zero_grad_stats comes from a query call.
  *  - Device calls are asynchronous and ordered on the caller's HIP stream,
  *    passed as `void *stream` (a hipStream_t; NULL is the null stream).  They
- *    never synchronise and never read device data on the host.  Argument
+ *    never synchronise and never read device data on the host, except the
+ *    calls that move data between device and host by design and say so:
+ *    zero_offload_adam_step, zero_ckpt_save and zero_ckpt_load.  Argument
  *    checks happen on the host before any launch; a launch failure reported
  *    by the runtime returns ZERO_EDEVICE.
  *  - Device pointers are plain device addresses (e.g. a torch tensor's
