@@ -100,6 +100,7 @@ class Workload:
         from synth import CONFIGS, gen
 
         self.z, self.torch = z, torch
+        self.cfg_idx = cfg_idx
         cfg = self.cfg = CONFIGS[cfg_idx]
         self.dev = device
         self.begin, self.end = z.zero_partition(cfg.psi, cfg.nd, cfg.rank)
@@ -199,6 +200,57 @@ def cpu_baseline(w, target_s: float = 12.0):
             "kind": "oracle",
             "sample": f"first {k} elements of the same shard in host memory, fp64 grad stats "
                       f"+ AdamW, {reps} pass(es) in {total:.1f} s"}
+
+
+_ONE_THREAD_SCRIPT = """
+import json, sys, time
+import numpy as np
+sys.path.insert(0, sys.argv[1])
+import oracle
+from synth import CONFIGS
+cfg = CONFIGS[int(sys.argv[2])]
+a = np.load(sys.argv[3])
+g, th, m, v, p = (a[k].copy() for k in ("g", "th", "m", "v", "p"))
+total, reps = 0.0, 0
+while total < float(sys.argv[4]):
+    t0 = time.perf_counter()
+    sq, ov = oracle.grad_stats(g, cfg.dtype, cfg.hp.inv_loss_scale)
+    s = oracle.step_scalars(cfg.hp, True, sq, ov, 0)
+    oracle.adamw_(s, g, cfg.dtype, th, m, v, p, cfg.dtype)
+    total += time.perf_counter() - t0
+    reps += 1
+print(json.dumps({"threads": oracle.num_threads(), "n": int(g.size), "reps": reps, "s": total}))
+"""
+
+
+def cpu_baseline_one_thread(w, k: int = 1 << 24, target_s: float = 4.0):
+    """The same oracle pass on one host thread (a child process started with
+    OMP_NUM_THREADS=1), on the first k elements of the shard, repeated for
+    about target_s seconds; plus the host's CPU model and memory."""
+    import subprocess
+    import tempfile
+    k = min(k, w.n)
+
+    def host(t, np_dt):
+        return t[:k].cpu().numpy().view(np_dt).copy()
+
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "sample.npz")
+        np.savez(path, g=host(w.g, np.uint16), th=host(w.master, np.float32),
+                 m=host(w.m, np.float32), v=host(w.v, np.float32), p=np.zeros(k, np.uint16))
+        env = dict(os.environ, OMP_NUM_THREADS="1")
+        out = subprocess.run([sys.executable, "-c", _ONE_THREAD_SCRIPT, ROOT, str(w.cfg_idx), path,
+                              str(target_s)], env=env, capture_output=True, text=True,
+                             timeout=300, check=True).stdout
+    r = json.loads(out.strip().splitlines()[-1])
+    cpu = next((l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
+                if l.startswith("model name")), "unknown")
+    mem_kb = next((int(l.split()[1]) for l in open("/proc/meminfo") if l.startswith("MemTotal")), 0)
+    return {"value": r["n"] * r["reps"] / r["s"], "unit": "params/s", "cores": r["threads"],
+            "kind": "oracle",
+            "sample": f"first {r['n']} elements of the same shard, fp64 grad stats + AdamW, "
+                      f"{r['reps']} pass(es) in {r['s']:.1f} s",
+            "host_cpu": cpu, "host_mem_gb": round(mem_kb / 1e6, 1)}
 
 
 def load_traffic(n_params: int):
@@ -575,6 +627,8 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
         out["cpu_baseline"] = cpu_baseline(w)
+        log("[bench] timing the oracle on one host thread")
+        out["cpu_baseline_one_thread"] = cpu_baseline_one_thread(w)
     print(json.dumps(out), flush=True)
 
 
