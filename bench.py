@@ -518,8 +518,9 @@ def main():
                     help="time grad stats and AdamW alone on every workload of >= 100M params")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one data-parallel rank's shard on one GPU; runs on more "
-              "than one GPU are not supported by this build", file=sys.stderr)
+        print("bench.py measures one data-parallel rank's shard on one GPU; it does not "
+              "run on more than one GPU (the exchanges between ranks are not implemented)",
+              file=sys.stderr)
         sys.exit(2)
 
     if args.copy_probe:

@@ -1,5 +1,5 @@
 """bench.py's contract on the host: a run on more than one GPU exits with a
-message before any device work (the build measures one GPU)."""
+message before any device work (the bench measures one GPU)."""
 import os
 import subprocess
 import sys
