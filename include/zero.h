@@ -127,6 +127,8 @@ zero_status zero_bucket_plan(const uint64_t *numel, uint32_t n_tensors, uint64_t
  * are therefore spread evenly: offsets[i] = i * step, with step a multiple of
  * 2 MiB and 4 * step + 2n + 16 <= pool_bytes, so every array may also be
  * shifted by up to 16 bytes (a 16-bit shard's phase in its flat buffer).
+ * The rest of the pool stays the caller's: other buffers placed in the gaps
+ * (per-tensor gradients, say) leave the step's speed unchanged.
  * Errors: ZERO_EINVAL (NULL offsets, n too large), ZERO_ENOSPC (the pool is
  * too small for non-overlapping arrays: step < 4n + 16). */
 zero_status zero_state_layout(uint64_t n, uint64_t pool_bytes, uint64_t offsets[5]);
