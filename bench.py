@@ -509,6 +509,8 @@ def main():
                     help="gather per fused buffer, then a separate statistics pass")
     ap.add_argument("--offload", action="store_true",
                     help="time the step with the optimizer state in host memory instead")
+    ap.add_argument("--chunk", type=int, default=1 << 24,
+                    help="with --offload: elements per pinned staging slot")
     ap.add_argument("--ckpt", action="store_true",
                     help="time a sharded checkpoint save and load of one rank's state instead")
     ap.add_argument("--separate", action="store_true",
@@ -527,7 +529,7 @@ def main():
         copy_probe(args.steps)
         return
     if args.offload:
-        offload_bench(args.config, args.steps, args.warmup)
+        offload_bench(args.config, args.steps, args.warmup, chunk=args.chunk)
         return
     if args.ckpt:
         ckpt_bench()
