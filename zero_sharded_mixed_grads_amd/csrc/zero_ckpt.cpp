@@ -107,6 +107,44 @@ zero_status hip_check(hipError_t e, const char *what)
     return ZERO_OK;
 }
 
+// Two pinned host slots of `slot` bytes with one event each, so that the copy
+// of one chunk between device and host overlaps the file I/O of the other.
+// The destructor drains the stream before freeing the slots: no copy queued
+// into or out of them outlives the call, also on an error path.
+struct Staging {
+    hipStream_t stream;
+    size_t slot = 0;
+    char *buf = nullptr;
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    explicit Staging(hipStream_t s) : stream(s) {}
+    ~Staging()
+    {
+        (void)hipStreamSynchronize(stream);
+        for (hipEvent_t e : ev)
+            if (e)
+                (void)hipEventDestroy(e);
+        if (buf)
+            (void)hipHostFree(buf);
+    }
+    zero_status init(size_t bytes, const char *what)
+    {
+        slot = bytes;
+        zero_status st = hip_check(hipHostMalloc((void **)&buf, 2 * bytes, hipHostMallocDefault),
+                                   what);
+        for (int i = 0; i < 2 && st == ZERO_OK; ++i)
+            st = hip_check(hipEventCreateWithFlags(&ev[i], hipEventDisableTiming), what);
+        return st;
+    }
+    char *at(uint64_t k) const { return buf + (k % 2) * slot; }
+};
+
+// One staged piece of an array: `len` bytes at byte offset `off`.
+struct Piece {
+    int array;
+    uint64_t off;
+    size_t len;
+};
+
 }  // namespace
 
 extern "C" zero_status zero_ckpt_save(const char *path, uint64_t psi, uint32_t nd, uint32_t rank,
@@ -153,19 +191,35 @@ extern "C" zero_status zero_ckpt_save(const char *path, uint64_t psi, uint32_t n
     TmpFile guard{tmp};
     if (!write_all(f.fd, &h, sizeof h))
         return fail(ZERO_EIO, "zero_ckpt_save: writing %s: %s", tmp.c_str(), strerror(errno));
-    std::vector<char> buf((size_t)std::min<uint64_t>(kChunk, std::max<uint64_t>(4 * n, 1)));
-    for (const float *arr : {master, exp_avg, exp_avg_sq}) {
-        for (uint64_t off = 0; off < 4 * n; off += buf.size()) {
-            const size_t len = (size_t)std::min<uint64_t>(buf.size(), 4 * n - off);
-            if ((st = hip_check(hipMemcpyAsync(buf.data(), (const char *)arr + off, len,
-                                               hipMemcpyDeviceToHost, s),
-                                "zero_ckpt_save: copy to host")) != ZERO_OK ||
-                (st = hip_check(hipStreamSynchronize(s), "zero_ckpt_save: stream")) != ZERO_OK)
-                return st;
-            if (!write_all(f.fd, buf.data(), len))
-                return fail(ZERO_EIO, "zero_ckpt_save: writing %s: %s", tmp.c_str(),
-                            strerror(errno));
-        }
+    // the arrays in chunks through two pinned slots: the copy of chunk k + 1 to
+    // the host runs while chunk k is written to the file
+    const float *arrays[3] = {master, exp_avg, exp_avg_sq};
+    std::vector<Piece> pieces;
+    for (int a = 0; a < 3; ++a)
+        for (uint64_t off = 0; off < 4 * n; off += kChunk)
+            pieces.push_back({a, off, (size_t)std::min<uint64_t>(kChunk, 4 * n - off)});
+    Staging stg(s);
+    if (!pieces.empty() &&
+        (st = stg.init((size_t)std::min<uint64_t>(kChunk, 4 * n), "zero_ckpt_save: staging")) !=
+            ZERO_OK)
+        return st;
+    auto fetch = [&](uint64_t k) -> zero_status {
+        const Piece &q = pieces[k];
+        zero_status r = hip_check(hipMemcpyAsync(stg.at(k), (const char *)arrays[q.array] + q.off,
+                                                 q.len, hipMemcpyDeviceToHost, s),
+                                  "zero_ckpt_save: copy to host");
+        return r != ZERO_OK ? r : hip_check(hipEventRecord(stg.ev[k % 2], s), "zero_ckpt_save");
+    };
+    if (!pieces.empty() && (st = fetch(0)) != ZERO_OK)
+        return st;
+    for (uint64_t k = 0; k < pieces.size(); ++k) {
+        if (k + 1 < pieces.size() && (st = fetch(k + 1)) != ZERO_OK)
+            return st;
+        if ((st = hip_check(hipEventSynchronize(stg.ev[k % 2]), "zero_ckpt_save: copy to host")) !=
+            ZERO_OK)
+            return st;
+        if (!write_all(f.fd, stg.at(k), pieces[k].len))
+            return fail(ZERO_EIO, "zero_ckpt_save: writing %s: %s", tmp.c_str(), strerror(errno));
     }
     if (d_scale && !write_all(f.fd, &scale, sizeof scale))
         return fail(ZERO_EIO, "zero_ckpt_save: writing %s: %s", tmp.c_str(), strerror(errno));
@@ -283,7 +337,15 @@ extern "C" zero_status zero_ckpt_load(const char *const *paths, uint32_t n_paths
     hipStream_t s = (hipStream_t)stream;
     if ((st = hip_check(hipStreamSynchronize(s), "zero_ckpt_load: stream")) != ZERO_OK)
         return st;
-    std::vector<char> buf((size_t)std::min<uint64_t>(kChunk, std::max<uint64_t>(4 * n, 1)));
+    // chunks through two pinned slots: chunk k is read from its file while the
+    // copy of chunk k - 1 to the device runs; a slot is refilled only after its
+    // previous copy has finished
+    Staging stg(s);
+    if (n > 0 && (st = stg.init((size_t)std::min<uint64_t>(kChunk, 4 * n),
+                                "zero_ckpt_load: staging")) != ZERO_OK)
+        return st;
+    float *dsts[3] = {master, exp_avg, exp_avg_sq};
+    uint64_t k = 0;  // chunks staged so far
     for (uint32_t i : order) {
         const uint64_t lo = std::max(begin, hs[i].begin), hi = std::min(end, hs[i].end);
         if (lo >= hi)
@@ -293,18 +355,20 @@ extern "C" zero_status zero_ckpt_load(const char *const *paths, uint32_t n_paths
         if (f.fd < 0)
             return fail(ZERO_EIO, "zero_ckpt_load: cannot open %s: %s", paths[i], strerror(errno));
         const uint64_t file_n = hs[i].end - hs[i].begin;
-        float *dsts[3] = {master, exp_avg, exp_avg_sq};
         for (int a = 0; a < 3; ++a) {
             const uint64_t src0 = sizeof(zero_ckpt_header) + 4 * (a * file_n + (lo - hs[i].begin));
             char *dst0 = (char *)dsts[a] + 4 * (lo - begin);
-            for (uint64_t off = 0; off < 4 * (hi - lo); off += buf.size()) {
-                const size_t len = (size_t)std::min<uint64_t>(buf.size(), 4 * (hi - lo) - off);
-                if (!read_at(f.fd, buf.data(), len, src0 + off))
+            for (uint64_t off = 0; off < 4 * (hi - lo); off += stg.slot, ++k) {
+                const size_t len = (size_t)std::min<uint64_t>(stg.slot, 4 * (hi - lo) - off);
+                if (k >= 2 && (st = hip_check(hipEventSynchronize(stg.ev[k % 2]),
+                                              "zero_ckpt_load: copy to device")) != ZERO_OK)
+                    return st;
+                if (!read_at(f.fd, stg.at(k), len, src0 + off))
                     return fail(ZERO_EIO, "zero_ckpt_load: reading %s", paths[i]);
-                if ((st = hip_check(hipMemcpyAsync(dst0 + off, buf.data(), len,
+                if ((st = hip_check(hipMemcpyAsync(dst0 + off, stg.at(k), len,
                                                    hipMemcpyHostToDevice, s),
                                     "zero_ckpt_load: copy to device")) != ZERO_OK ||
-                    (st = hip_check(hipStreamSynchronize(s), "zero_ckpt_load: stream")) != ZERO_OK)
+                    (st = hip_check(hipEventRecord(stg.ev[k % 2], s), "zero_ckpt_load")) != ZERO_OK)
                     return st;
             }
         }
