@@ -265,21 +265,35 @@ def load_traffic(n_params: int):
 
 
 def copy_probe(steps: int):
-    """Plain device copies of a known size: the achievable streaming ceiling
-    (read + write, like the AdamW step) and the reference dispatch for
-    calibrating the HBM byte counters.  Prints one JSON line."""
+    """Streaming kernels of a known size: plain copies (the achievable ceiling
+    for a read + write mix like the AdamW step, and the reference dispatch for
+    calibrating the HBM byte counters), plus a write-only fill, an in-place
+    read-modify-write and a read-only pass.  Prints one JSON line."""
     import torch
     n = 1 << 30  # fp32 elements: 4 GiB read + 4 GiB written per copy
     src = torch.empty(n, dtype=torch.float32, device="cuda:0").normal_()
     dst = torch.empty_like(src)
     import zero_sharded_mixed_grads_amd as z
     res = {}
-    for name, fn in (("copy_", lambda: dst.copy_(src)),
-                     ("mul_out", lambda: torch.mul(src, 1.0, out=dst)),
-                     # the library's own gather of one aligned fp32 tensor: a plain copy
-                     # with the same 16-byte load/store pattern as the path's kernels
-                     ("zero_bucket_flatten", lambda: z.zero_bucket_flatten([src], [n], "f32", 0,
-                                                                           n, dst))):
+    g16 = src.view(torch.float16)  # the same 4 GiB read as 2^31 fp16 gradients
+    stats = z.new_grad_stats(src.device)
+    ws = z.new_workspace(g16.numel(), src.device)
+    nb = 4 * n
+    for name, fn, rd, wr in (
+            ("copy_", lambda: dst.copy_(src), nb, nb),
+            ("mul_out", lambda: torch.mul(src, 1.0, out=dst), nb, nb),
+            # the library's own gather of one aligned fp32 tensor: a plain copy
+            # with the same 16-byte load/store pattern as the path's kernels
+            ("zero_bucket_flatten", lambda: z.zero_bucket_flatten([src], [n], "f32", 0, n, dst),
+             nb, nb),
+            # other access mixes: write only, read and write back in place (as
+            # AdamW does to master, m and v), and read only (the library's
+            # statistics pass over the buffer as fp16 gradients, and torch's sum)
+            ("fill_", lambda: dst.fill_(1.0), 0, nb),
+            ("mul_ in place", lambda: dst.mul_(1.0), nb, nb),
+            ("zero_grad_stats", lambda: z.zero_grad_stats(g16, "f16", g16.numel(), 1.0, ws,
+                                                          ws.numel(), stats), nb, 0),
+            ("sum", lambda: torch.sum(src), nb, 0)):
         fn()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -289,8 +303,8 @@ def copy_probe(steps: int):
         b.record()
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / steps
-        res[name] = {"ms": ms, "GB/s": 2 * 4 * n / (ms * 1e-3) / 1e9,
-                     "bytes_read": 4 * n, "bytes_written": 4 * n}
+        res[name] = {"ms": ms, "GB/s": (rd + wr) / (ms * 1e-3) / 1e9,
+                     "bytes_read": rd, "bytes_written": wr}
     print(json.dumps({"copy_probe": res}), flush=True)
 
 
