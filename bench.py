@@ -360,6 +360,22 @@ def configs_sweep(steps: int, warmup: int, spread: bool = True):
         st = z.read_adam_state(state)
         if st.skip or st.step != warmup + steps:
             raise SystemExit(f"{cfg.name}: a step was skipped; timing would be invalid")
+        # the skip path: one non-finite gradient, then AdamW writes nothing
+        g[0] = float("inf")
+        calls["grad_stats"]()
+        ms = []
+        for _ in range(steps):
+            a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            calls["adam_step"]()
+            c.record()
+            ms.append((a, c))
+        torch.cuda.synchronize()
+        ms = sorted(x.elapsed_time(y) for x, y in ms)
+        st = z.read_adam_state(state)
+        if not st.skip or st.step != warmup + steps:
+            raise SystemExit(f"{cfg.name}: the overflowing steps were not skipped")
+        res["adam_step_skipped"] = {"ms_median": ms[len(ms) // 2], "ms_min": ms[0]}
         out[cfg.name] = res
         log(f"[bench] {cfg.name}: n={n} adam {res['adam_step']['ms_median']:.3f} ms "
             f"({res['adam_step']['GB/s']:.0f} GB/s)")
