@@ -129,7 +129,9 @@ class Workload:
         nb = z.zero_bucket_flatten_stats_workspace(cfg.numels, self.begin, n)
         self.fws = torch.empty(nb, dtype=torch.uint8, device=device)
         self.hp = z.adamw(**cfg.hp.__dict__)
-        self.ptrs = [t.data_ptr() if t is not None else None for t in self.grads]
+        # the gradient table, marshalled once (self.grads keeps the tensors alive)
+        self.ptrs, self.numels = z.tensor_table(
+            [t.data_ptr() if t is not None else None for t in self.grads], cfg.numels)
         torch.cuda.synchronize()
         log(f"[bench] inputs resident in HBM after {time.time() - t0:.1f}s "
             f"({torch.cuda.memory_allocated() / 1e9:.1f} GB allocated)")
@@ -148,14 +150,14 @@ class Workload:
         b, e = z.zero_partition(cfg.psi, cfg.nd, cfg.rank)
         B = cfg.bucket_elems or cfg.psi
         if fused:
-            z.zero_bucket_flatten_stats(self.ptrs, cfg.numels, cfg.dtype, b, e - b, self.g,
+            z.zero_bucket_flatten_stats(self.ptrs, self.numels, cfg.dtype, b, e - b, self.g,
                                         cfg.hp.inv_loss_scale, self.fws, self.fws.numel(),
                                         self.stats, s)
         else:
             lo = b
             while lo < e:  # one fused buffer at a time, this rank's part of it
                 hi = min((lo // B + 1) * B, e)
-                z.zero_bucket_flatten(self.ptrs, cfg.numels, cfg.dtype, lo, hi - lo,
+                z.zero_bucket_flatten(self.ptrs, self.numels, cfg.dtype, lo, hi - lo,
                                       self.g.data_ptr() + 2 * (lo - b), s)
                 lo = hi
             if marks: marks[0].record(stream)
@@ -312,7 +314,9 @@ def configs_sweep(steps: int, warmup: int, spread: bool = True):
     """zero_grad_stats and zero_adam_step timed alone on the flat shard of each
     workload of at least 100M parameters (1.5B at Nd 1, 7.5B rank 3 of 8, 13B
     at Nd 1, 100B rank 399 of 400), with the 16-bit arrays at the element
-    phase the shard has in the flat layout.  Prints one JSON line."""
+    phase the shard has in the flat layout; then a skipped (overflowing) step,
+    and the fused gather + statistics of the shard from its per-tensor
+    gradients.  Prints one JSON line."""
     import torch
     import zero_sharded_mixed_grads_amd as z
     from synth import CONFIGS, gen
@@ -376,9 +380,47 @@ def configs_sweep(steps: int, warmup: int, spread: bool = True):
         if not st.skip or st.step != warmup + steps:
             raise SystemExit(f"{cfg.name}: the overflowing steps were not skipped")
         res["adam_step_skipped"] = {"ms_median": ms[len(ms) // 2], "ms_min": ms[0]}
+        # the fused gather + statistics of the shard from its per-tensor gradients,
+        # each tensor that meets the shard in an allocation of its own
+        starts = np.cumsum([0] + list(cfg.numels))
+        which = [i for i in range(len(cfg.numels)) if starts[i] < e and starts[i + 1] > b]
+        try:
+            grads = gen.device_grad_list(cfg, 1, dev, which)
+        except torch.OutOfMemoryError:
+            grads = None
+            res["gather_stats"] = "not measured: no room for the per-tensor gradients"
+        if grads is not None:
+            ptrs, nums = z.tensor_table([grads.get(i) for i in range(len(cfg.numels))],
+                                        cfg.numels)
+            fws_n = z.zero_bucket_flatten_stats_workspace(nums, b, n)
+            fws = torch.empty(fws_n, dtype=torch.uint8, device=dev)
+
+            def gather():
+                z.zero_bucket_flatten_stats(ptrs, nums, cfg.dtype, b, n, g,
+                                            cfg.hp.inv_loss_scale, fws, fws_n, stats)
+            for _ in range(warmup):
+                gather()
+            torch.cuda.synchronize()
+            evs = []
+            for _ in range(steps):
+                a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                gather()
+                c.record()
+                evs.append((a, c))
+            torch.cuda.synchronize()
+            ms = sorted(x.elapsed_time(y) for x, y in evs)
+            med = ms[len(ms) // 2]
+            res["gather_stats"] = {"tensors": len(which), "ms_median": med, "ms_min": ms[0],
+                                   "GB/s": FLATTEN_BYTES_PER_PARAM * n / med / 1e6,
+                                   "frac": FLATTEN_BYTES_PER_PARAM * n / med / 1e6 / HBM_PEAK_GBS}
+            del grads, ptrs, nums, fws
         out[cfg.name] = res
+        gs = res["gather_stats"]
         log(f"[bench] {cfg.name}: n={n} adam {res['adam_step']['ms_median']:.3f} ms "
-            f"({res['adam_step']['GB/s']:.0f} GB/s)")
+            f"({res['adam_step']['GB/s']:.0f} GB/s); gather+stats "
+            + (f"{gs['ms_median']:.3f} ms ({gs['GB/s']:.0f} GB/s, {gs['tensors']} tensors)"
+               if isinstance(gs, dict) else gs))
         del gbuf, pbuf, g, p, master, m, v, ws, calls
         torch.cuda.empty_cache()
     print(json.dumps({"configs": out}), flush=True)

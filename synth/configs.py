@@ -12,7 +12,9 @@ That gives 12*h*h + 13*h parameters per layer.
 
 Only shapes, dtypes, seeds and hyper-parameters are stated here.
 """
+import math
 from dataclasses import dataclass, field
+from functools import cached_property
 from typing import List, Optional, Tuple
 
 import numpy as np
@@ -79,9 +81,9 @@ class Config:
     inject: bool = False        # one step of the run carries inf/nan grads
     host_generated: bool = False  # small enough to draw every input on the host
 
-    @property
+    @cached_property
     def numels(self) -> List[int]:
-        return [int(np.prod(s)) for _, s in self.tensors]
+        return [math.prod(s) for _, s in self.tensors]
 
     @property
     def psi(self) -> int:

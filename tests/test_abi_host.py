@@ -335,3 +335,16 @@ def test_state_layout():
     assert z.zero_state_layout(n, need)[1] >= 4 * n + 16
     with pytest.raises(z.ZeroError):
         z.zero_state_layout(n, need - 1)
+
+
+def test_tensor_table_marshals_once_and_checks_lengths():
+    """The binding's pre-marshalled gather table: pointers (None for tensors
+    outside the range) and element counts as C arrays, passed through
+    unchanged when given again; mismatched lengths are refused."""
+    ptrs, nums = z.tensor_table([0x1000, None, 0x2000], [3, 5, 7])
+    assert list(ptrs) == [0x1000, None, 0x2000] and list(nums) == [3, 5, 7]
+    assert z.tensor_table(ptrs, nums) == (ptrs, nums)
+    assert z.zero_bucket_flatten_stats_workspace(nums, 0, 15) == \
+        z.zero_bucket_flatten_stats_workspace([3, 5, 7], 0, 15)
+    with pytest.raises(ValueError):
+        z.tensor_table([0x1000, None], [3, 5, 7])

@@ -197,15 +197,31 @@ def zero_state_layout(n: int, pool_bytes: int) -> List[int]:
 
 
 # ------------------------------------------------------------- device calls
+def tensor_table(tensors: Sequence, numel: Optional[Sequence[int]] = None):
+    """The (pointer array, element-count array) pair that the gather calls
+    take, marshalled once.  tensors: device tensors or device pointers (None
+    for tensors outside the range); numel defaults to each tensor's numel().
+    Passing the pair to the gathers as `tensors` and `numel` skips building
+    the two arrays again on every call, which costs about 0.1 ms per
+    thousand tensors."""
+    if isinstance(tensors, ctypes.Array) and isinstance(numel, ctypes.Array):
+        return tensors, numel
+    if numel is None:
+        numel = [t.numel() for t in tensors]
+    if len(numel) != len(tensors):
+        raise ValueError(f"{len(tensors)} tensors but {len(numel)} element counts")
+    ptrs = (VP * len(tensors))(*[_ptr(t) for t in tensors])
+    nums = (U64 * len(numel))(*numel)
+    return ptrs, nums
+
+
 def zero_bucket_flatten(tensors: Sequence, numel: Optional[Sequence[int]], dtype,
                         range_begin: int, count: int, dst, stream=None) -> None:
     """tensors: device tensors or device pointers (None allowed for tensors
-    outside the range); numel defaults to each tensor's numel()."""
-    if numel is None:
-        numel = [t.numel() for t in tensors]
-    ptrs = (VP * len(tensors))(*[_ptr(t) for t in tensors])
-    nums = (U64 * len(numel))(*numel)
-    _check(lib().zero_bucket_flatten(ptrs, nums, len(tensors), _dtype(dtype), range_begin,
+    outside the range); numel defaults to each tensor's numel().  Both may
+    also be the arrays of tensor_table()."""
+    ptrs, nums = tensor_table(tensors, numel)
+    _check(lib().zero_bucket_flatten(ptrs, nums, len(ptrs), _dtype(dtype), range_begin,
                                      count, _ptr(dst), _stream(stream)))
 
 
@@ -225,7 +241,7 @@ def zero_grad_stats(grad, gdtype, n: int, inv_loss_scale: float, workspace, ws_b
 
 def zero_bucket_flatten_stats_workspace(numel: Sequence[int], range_begin: int,
                                         count: int) -> int:
-    nums = (U64 * len(numel))(*numel)
+    nums = numel if isinstance(numel, ctypes.Array) else (U64 * len(numel))(*numel)
     out = ctypes.c_size_t()
     _check(lib().zero_bucket_flatten_stats_workspace(nums, len(numel), range_begin, count,
                                                      ctypes.byref(out)))
@@ -236,11 +252,9 @@ def zero_bucket_flatten_stats(tensors: Sequence, numel: Optional[Sequence[int]],
                               range_begin: int, count: int, dst, inv_loss_scale: float,
                               workspace, ws_bytes: int, d_stats, stream=None,
                               d_scale=None) -> None:
-    if numel is None:
-        numel = [t.numel() for t in tensors]
-    ptrs = (VP * len(tensors))(*[_ptr(t) for t in tensors])
-    nums = (U64 * len(numel))(*numel)
-    _check(lib().zero_bucket_flatten_stats(ptrs, nums, len(tensors), _dtype(gdtype), range_begin,
+    """tensors and numel as for zero_bucket_flatten."""
+    ptrs, nums = tensor_table(tensors, numel)
+    _check(lib().zero_bucket_flatten_stats(ptrs, nums, len(ptrs), _dtype(gdtype), range_begin,
                                            count, _ptr(dst), inv_loss_scale, _ptr(d_scale),
                                            _ptr(workspace), ws_bytes, _ptr(d_stats),
                                            _stream(stream)))
