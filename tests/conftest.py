@@ -14,6 +14,7 @@ def pytest_configure(config):
 def pytest_sessionstart(session):
     import util
     util._reporter = session.config.pluginmanager.getplugin("terminalreporter")
+    util._capman = session.config.pluginmanager.getplugin("capturemanager")
 
 
 import pytest  # noqa: E402
@@ -21,7 +22,7 @@ import pytest  # noqa: E402
 
 @pytest.fixture(autouse=True)
 def _announce_gpu_case(request):
-    """Names each GPU case on the real stderr before it runs, so that a run
+    """Names each GPU case on the terminal before it runs, so that a run
     that ends abruptly still says which case was running."""
     if request.node.get_closest_marker("gpu") is not None:
         import util

@@ -1,6 +1,8 @@
 """Helpers shared by the GPU parity tests: phase-controlled device buffers
 with canary guard bands, 16-bit ordered distance, and the AdamW comparison
 criteria (per-step bounds scaled by the size of each update's terms)."""
+import sys
+
 import numpy as np
 import torch
 
@@ -152,13 +154,17 @@ class FreeRunScales:
 
 
 _reporter = None  # pytest's terminal reporter, set by conftest
+_capman = None    # pytest's capture manager, set by conftest
 
 
 def progress(msg):
-    """A progress line that reaches the terminal even while output is captured."""
+    """A progress line that reaches the terminal even while output is captured.
+    pytest captures file descriptors 1 and 2 during a test, the terminal
+    reporter's own writes included, so capture is suspended around the write."""
     line = f"    [progress] {msg}"
-    if _reporter is not None:
-        _reporter.write_line(line)
-        _reporter._tw.flush()
+    if _reporter is not None and _capman is not None:
+        with _capman.global_and_fixture_disabled():
+            _reporter.write_line(line)
+            _reporter._tw.flush()
     else:
-        print(line, flush=True)
+        print(line, file=sys.stderr, flush=True)
