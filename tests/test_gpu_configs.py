@@ -155,7 +155,7 @@ def test_workload1_tiny_full(fused):
     assert np.array_equal(r.master.cpu().numpy().view(np.uint32), th_o.view(np.uint32))
     m_o, v_o, p_o = np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, NP16)
     scales = FreeRunScales(cfg.hp, th_o)
-    worst = {}
+    worst, worst1, norm_rel, far = {}, {}, 0.0, [0, 0]
     for k in range(cfg.steps):
         host = gen.host_grad_list(cfg, k)
         grads = {i: torch.from_numpy(h.view(np.int16)).to(dev()) for i, h in enumerate(host)}
@@ -171,6 +171,7 @@ def test_workload1_tiny_full(fused):
         st = z.read_grad_stats(r.stats)
         sq, ov = oracle.grad_stats(g_ref, cfg.dtype, cfg.hp.inv_loss_scale)
         assert st.overflow == ov == 0 and abs(st.sq_norm - sq) <= 1e-5 * sq
+        norm_rel = max(norm_rel, abs(st.sq_norm - sq) / sq)
         gv = oracle.value16(g_ref, cfg.dtype)
         # one-step mode
         s1 = oracle.step_scalars(cfg.hp, True, st.sq_norm, st.overflow, k)
@@ -180,16 +181,21 @@ def test_workload1_tiny_full(fused):
         p_g = _to_host16(r.p)
         e1 = check_adam_one_step(cfg.hp, s1, gv, th0, m0, v0, th_g, m_g, v_g, th1, m1, v1,
                                  label=f"step {k}")
-        check_params16(p_g, th_g, th1, e1.pop("master_scale"), 1e-6, cfg.dtype, f"step {k}")
+        far[0] = max(far[0], check_params16(p_g, th_g, th1, e1.pop("master_scale"), 1e-6,
+                                            cfg.dtype, f"step {k}"))
+        worst1 = {key: max(worst1.get(key, 0), val) for key, val in e1.items()}
         # free-running
         s = oracle.step_scalars(cfg.hp, True, sq, ov, k)
         oracle.adamw_(s, g_ref, cfg.dtype, th_o, m_o, v_o, p_o, cfg.dtype)
         scales.update(s, gv, m_o, v_o)
         errs = scales.check(th_g, m_g, v_g, th_o, m_o, v_o, label=f"step {k}")
-        check_params16(p_g, th_g, th_o, errs.pop("master_scale"), 1e-5, cfg.dtype, f"step {k}")
+        far[1] = max(far[1], check_params16(p_g, th_g, th_o, errs.pop("master_scale"), 1e-5,
+                                            cfg.dtype, f"step {k}"))
         worst = {key: max(worst.get(key, 0), val) for key, val in errs.items()}
     assert z.read_adam_state(r.state).step == cfg.steps
-    progress(f"workload 1: worst free-running error / scale {worst}")
+    progress(f"workload 1 {'fused' if fused else 'unfused'}: {cfg.steps} steps, worst norm "
+             f"rel.err {norm_rel:.1e}, worst error / scale one-step {worst1} free {worst}, "
+             f"params beyond 1 ulp: {far[0]}/{far[1]} of {n}")
 
 
 # ------------------------------------------------------------ workload 5
@@ -258,7 +264,8 @@ def test_workload5_shard_skip_full(fused):
         oracle.adamw_(s1, g_ref, cfg.dtype, th1, m1, v1, p1, cfg.dtype)
         e1 = check_adam_one_step(cfg.hp, s1, gv, th0, m0, v0, th_g, m_g, v_g, th1, m1, v1,
                                  label=f"step {k}")
-        check_params16(p_g, th_g, th1, e1.pop("master_scale"), 1e-6, cfg.dtype, f"step {k}")
+        far1 = check_params16(p_g, th_g, th1, e1.pop("master_scale"), 1e-6, cfg.dtype,
+                              f"step {k}")
         del th1, m1, v1, p1
         s = oracle.step_scalars(cfg.hp, True, sq, ov, t_expect - 1)
         oracle.adamw_(s, g_ref, cfg.dtype, th_o, m_o, v_o, p_o, cfg.dtype)
@@ -266,8 +273,9 @@ def test_workload5_shard_skip_full(fused):
         e2 = scales.check(th_g, m_g, v_g, th_o, m_o, v_o, label=f"step {k}")
         far = check_params16(p_g, th_g, th_o, e2.pop("master_scale"), 1e-5, cfg.dtype,
                              f"step {k}")
-        progress(f"workload 5 step {k}: sq {st.sq_norm:.9e} (oracle {sq:.9e}) one-step {e1} "
-                 f"free {e2} params beyond 1 ulp: {far}")
+        rel = abs(st.sq_norm - sq) / sq
+        progress(f"workload 5 step {k}: sq {st.sq_norm:.9e} rel.err {rel:.1e} one-step {e1} "
+                 f"free {e2} params beyond 1 ulp: {far1}/{far} of {n}")
         del grads
     assert t_expect == cfg.steps - 1
     # the 16-bit lead pad before the phase-faithful slice was never written
