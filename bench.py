@@ -17,6 +17,9 @@ Prints one JSON line.  `value` is parameters per second of the whole step
 (32 B/param fused, 34 unfused);
 the roofline object covers the fused AdamW kernel (28 algorithmic bytes per
 parameter: read grad 2 + master/m/v 12, write master/m/v 12 + param 2).
+copy_ceiling times the library's own plain copy of 4 GiB in the same process
+after the timed steps, and gives AdamW's and the whole step's bandwidth as
+fractions of it.
 """
 import argparse
 import hashlib
@@ -264,6 +267,37 @@ def load_traffic(n_params: int):
     if d.get("kernel_source_sha256_16") != kernel_source_hash() or d.get("n") != n_params:
         return None
     return d.get("bytes_per_launch")
+
+
+def copy_ceiling(device, reps: int = 20):
+    """The part's streaming ceiling for a read + write mix, measured in this
+    process: the library's own gather of one aligned 4 GiB fp32 tensor (a
+    plain copy with the path's 16-byte access pattern), median of reps calls.
+    None when the device has no room for the two buffers."""
+    import torch
+    import zero_sharded_mixed_grads_amd as z
+    n = 1 << 30
+    try:
+        src = torch.empty(n, dtype=torch.float32, device=device)
+        dst = torch.empty_like(src)
+    except torch.OutOfMemoryError:
+        return None
+    src.fill_(1.0)
+    for _ in range(3):
+        z.zero_bucket_flatten([src], [n], "f32", 0, n, dst)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(reps):
+        z.zero_bucket_flatten([src], [n], "f32", 0, n, dst)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]))
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"kernel": "zero_bucket_flatten of one aligned 4 GiB fp32 tensor (a plain copy)",
+            "ms": ms, "GB/s": 8 * n / (ms * 1e-3) / 1e9}
 
 
 def copy_probe(steps: int):
@@ -699,6 +733,14 @@ def main():
         "checks": {"device_steps_taken": int(st.step), "overflow": int(gs.overflow),
                    "sq_norm": gs.sq_norm, "clip_coef": st.coef},
     }
+    # the same process's copy ceiling, for the fraction of what a plain copy reaches
+    cc = copy_ceiling(dev)
+    if cc is not None:
+        cc["adam_frac_of_copy"] = adam_gbs / cc["GB/s"]
+        cc["step_frac_of_copy"] = step_bytes * n / (step_ms * 1e-3) / 1e9 / cc["GB/s"]
+        log(f"[bench] copy ceiling {cc['GB/s']:.0f} GB/s; AdamW at "
+            f"{cc['adam_frac_of_copy']:.3f} of it")
+    out["copy_ceiling"] = cc
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
         out["cpu_baseline"] = cpu_baseline(w)
