@@ -100,11 +100,11 @@ class Workload:
     def __init__(self, cfg_idx: int, device, spread: bool = True):
         import torch
         import zero_sharded_mixed_grads_amd as z
-        from synth import CONFIGS, gen
+        from synth import WORKLOADS, gen
 
         self.z, self.torch = z, torch
         self.cfg_idx = cfg_idx
-        cfg = self.cfg = CONFIGS[cfg_idx]
+        cfg = self.cfg = WORKLOADS[cfg_idx]
         self.dev = device
         self.begin, self.end = z.zero_partition(cfg.psi, cfg.nd, cfg.rank)
         n = self.n = self.end - self.begin
@@ -212,8 +212,8 @@ import json, sys, time
 import numpy as np
 sys.path.insert(0, sys.argv[1])
 import oracle
-from synth import CONFIGS
-cfg = CONFIGS[int(sys.argv[2])]
+from synth import WORKLOADS
+cfg = WORKLOADS[int(sys.argv[2])]
 a = np.load(sys.argv[3])
 g, th, m, v, p = (a[k].copy() for k in ("g", "th", "m", "v", "p"))
 total, reps = 0.0, 0
@@ -353,11 +353,11 @@ def configs_sweep(steps: int, warmup: int, spread: bool = True):
     gradients.  Prints one JSON line."""
     import torch
     import zero_sharded_mixed_grads_amd as z
-    from synth import CONFIGS, gen
+    from synth import WORKLOADS, gen
     dev = torch.device("cuda:0")
     out = {}
     for idx in (2, 3, 4, 5):
-        cfg = CONFIGS[idx]
+        cfg = WORKLOADS[idx]
         b, e = z.zero_partition(cfg.psi, cfg.nd, cfg.rank)
         n, ph = e - b, b % 8
         tdt = gen.torch_dtype(cfg.dtype)
@@ -471,8 +471,8 @@ def ckpt_bench(cfg_idx: int = 5, reps: int = 2):
     import tempfile
     import torch
     import zero_sharded_mixed_grads_amd as z
-    from synth import CONFIGS, gen
-    cfg = CONFIGS[cfg_idx]
+    from synth import WORKLOADS, gen
+    cfg = WORKLOADS[cfg_idx]
     dev = torch.device("cuda:0")
     b, e = z.zero_partition(cfg.psi, cfg.nd, cfg.rank)
     n = e - b
@@ -545,8 +545,8 @@ def offload_bench(cfg_idx: int, steps: int, warmup: int, chunk: int = 1 << 24):
     device, AdamW on the host cores.  Prints one JSON line."""
     import torch
     import zero_sharded_mixed_grads_amd as z
-    from synth import CONFIGS, gen
-    cfg = CONFIGS[cfg_idx]
+    from synth import WORKLOADS, gen
+    cfg = WORKLOADS[cfg_idx]
     dev = torch.device("cuda:0")
     b, e = z.zero_partition(cfg.psi, cfg.nd, cfg.rank)
     n = e - b

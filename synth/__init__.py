@@ -6,5 +6,5 @@ hyper-parameters) and *draws* them (seeded normal samples rounded to the
 partitioning, bucketing, statistics and the optimizer step live in the HIP
 library and, independently, in the oracle.
 """
-from .configs import CONFIGS, Config, AdamW, gpt_param_list, tiny_param_sizes  # noqa: F401
+from .configs import WORKLOADS, Config, AdamW, gpt_param_list, tiny_param_sizes  # noqa: F401
 from . import gen  # noqa: F401

@@ -137,4 +137,4 @@ def _gpt_100b_shard() -> Config:
         hp=AdamW(max_grad_norm=1.0, inv_loss_scale=1.0 / 65536.0), inject=True)
 
 
-CONFIGS = {c.idx: c for c in (_tiny(), _gpt2_1p5b(), _gpt_7p5b(), _gpt_13b(), _gpt_100b_shard())}
+WORKLOADS = {c.idx: c for c in (_tiny(), _gpt2_1p5b(), _gpt_7p5b(), _gpt_13b(), _gpt_100b_shard())}

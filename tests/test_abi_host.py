@@ -90,8 +90,8 @@ def test_bucket_plan_bit_exact(numels, bucket, data):
 
 
 def test_bucket_plan_workload_layout():
-    from synth import CONFIGS
-    cfg = CONFIGS[3]
+    from synth import WORKLOADS
+    cfg = WORKLOADS[3]
     b, e = oracle.partition(cfg.psi, cfg.nd, cfg.rank)
     B = cfg.bucket_elems
     nb = -(-cfg.psi // B)

@@ -26,7 +26,7 @@ import torch
 
 import oracle
 import zero_sharded_mixed_grads_amd as z
-from synth import CONFIGS, gen
+from synth import WORKLOADS, gen
 from util import FreeRunScales, check_adam_one_step, check_params16, dev, progress
 
 pytestmark = pytest.mark.gpu
@@ -143,7 +143,7 @@ def _oracle_norm_streamed(g_dev, dtype, inv, chunk=1 << 29):
 # ------------------------------------------------------------ workload 1
 @pytest.mark.parametrize("fused", [False, True])
 def test_workload1_tiny_full(fused):
-    cfg = CONFIGS[1]
+    cfg = WORKLOADS[1]
     r = Rank(cfg)
     n, b, e = r.n, r.begin, r.end
     assert (b, e, n) == (0, 262_144, 262_144)
@@ -206,7 +206,7 @@ def _w5_grads(cfg, r, step):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("fused", [False, True])
 def test_workload5_shard_skip_full(fused):
-    cfg = CONFIGS[5]
+    cfg = WORKLOADS[5]
     r = Rank(cfg, p_phase=oracle.partition(cfg.psi, cfg.nd, cfg.rank)[0] % 8)
     n, b = r.n, r.begin
     assert n == 250_728_263 and b % 8 == 1 and r.p.data_ptr() % 16 == 2
@@ -283,7 +283,7 @@ def test_workload5_shard_skip_full(fused):
 
 
 def test_workload5_single_nan_at_last_element():
-    cfg = CONFIGS[5]
+    cfg = WORKLOADS[5]
     r = Rank(cfg, p_phase=oracle.partition(cfg.psi, cfg.nd, cfg.rank)[0] % 8)
     gen.device_fill_normal_(r.master, cfg.master_seed(), cfg.master_sigma)
     r.gather(_w5_grads(cfg, r, 0))
@@ -371,7 +371,7 @@ def test_workload2_gpt2_1p5b_sampled(fused):
     """The bench's workload, launch configuration and state layout (fused:
     the bench's default step; unfused: one gather per 500M-element buffer,
     then stats)."""
-    cfg = CONFIGS[2]
+    cfg = WORKLOADS[2]
     r = Rank(cfg, spread=True)
     assert r.n == cfg.psi == 1_557_611_200
     gen.device_fill_normal_(r.master, cfg.master_seed(), cfg.master_sigma)
@@ -394,7 +394,7 @@ def test_workload2_gpt2_1p5b_sampled(fused):
 
 @pytest.mark.timeout(900)
 def test_workload3_gpt_7p5b_rank3_buckets_sampled():
-    cfg = CONFIGS[3]
+    cfg = WORKLOADS[3]
     r = Rank(cfg)
     assert (r.begin, r.end) == (2_797_398_528, 3_729_864_704)
     B = cfg.bucket_elems
@@ -435,7 +435,7 @@ def test_workload3_gpt_7p5b_rank3_buckets_sampled():
 
 @pytest.mark.timeout(900)
 def test_workload4_gpt_13b_full_state_sampled():
-    cfg = CONFIGS[4]
+    cfg = WORKLOADS[4]
     need = 16 * cfg.psi + (1 << 30)
     free, total = torch.cuda.mem_get_info()
     if free < need:
