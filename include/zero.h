@@ -275,12 +275,16 @@ typedef struct {
  * device from *d_stats, and inv = d_scale->inv_scale (read on the device)
  * when d_scale is not NULL, else hp->inv_loss_scale.  With dynamic loss
  * scaling, call zero_loss_scale_update after this call, on the same stream,
- * so that the step uses the scale its gradients were computed with.  If d_stats reports overflow, the step is skipped:
- * nothing is written to the arrays and `step` does not advance.
+ * so that the step uses the scale its gradients were computed with.  If
+ * d_stats reports overflow, the step is skipped: nothing is written to the
+ * arrays and `step` does not advance.
  * grad: n 16-bit gradients (gdt); master, exp_avg, exp_avg_sq: n fp32 each,
  * updated in place; param_out: n 16-bit params (pdt), written.  d_stats:
  * device result of zero_grad_stats (or NULL: no clipping, never skip);
  * d_state: device step state.  n == 0 still advances d_state.
+ * Occupancy: every block of the update reserves 64 KiB of LDS that it does
+ * not use, so that at most two blocks run per CU (of gfx950's 160 KiB);
+ * kernels that run beside it on other streams share the remaining LDS.
  * Errors: ZERO_EINVAL (NULL hp or d_state, NULL arrays with n > 0, bad
  * dtypes, lr < 0, beta outside [0, 1), eps <= 0, weight_decay < 0, no
  * d_scale and inv_loss_scale not finite and positive, NaN max_grad_norm,
