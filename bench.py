@@ -9,12 +9,17 @@ gradients already resident in HBM:
   -> zero_adam_step: fused AdamW on fp32 master/m/v, writes 16-bit params
 With --unfused the gather runs once per 500M-element fused buffer
 (zero_bucket_flatten) followed by a separate zero_grad_stats pass.
-Workload: GPT-2-1.5B-like parameter list (48 layers, hidden 1600, vocab
-50257, fp16) at Nd=1, so the rank's shard is all 1,557,611,200 parameters;
-loss scale 2^16, clip 1.0.
+Workload (default): the 13B-parameter GPT-style list (40 layers, hidden 5120,
+vocab 50257, bf16 grads and params) at Nd=1, so the rank's shard is all
+12,848,143,360 parameters and its whole 16-byte-per-parameter model state
+(205.6 GB) is resident in one MI355X's HBM; loss scale 1, no clipping.
+--config 2 runs the GPT-2-1.5B-like list (48 layers, hidden 1600, fp16) at
+Nd=1 instead (1,557,611,200 parameters, loss scale 2^16, clip 1.0).
 
 Prints one JSON line.  `value` is parameters per second of the whole step
-(32 B/param fused, 34 unfused);
+(32 B/param fused, 34 unfused); `step_tensors` times, after it, the step that
+reads the per-tensor gradients in place (zero_grad_stats_tensors, then
+zero_adam_step_tensors: 30 B/param) on the same workload;
 the roofline object covers the fused AdamW kernel (28 algorithmic bytes per
 parameter: read grad 2 + master/m/v 12, write master/m/v 12 + param 2).
 copy_ceiling times the library's own plain copy of 4 GiB in the same process
@@ -38,7 +43,8 @@ ADAM_BYTES_PER_PARAM = 28
 STATS_BYTES_PER_PARAM = 2
 FLATTEN_BYTES_PER_PARAM = 4  # 16-bit read + write
 METRIC = "Adam-shard params/sec + achieved HBM GB/s vs peak (28 B/param)"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "adamw_stream_gpt2-1.5b_traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
+CPU_SAMPLE_CAP = 1_000_000_000  # elements: the largest oracle sample (16 GB of host arrays)
 KERNEL_SRC = os.path.join(ROOT, "zero_sharded_mixed_grads_amd", "csrc", "zero_kernels.hip")
 
 
@@ -67,20 +73,25 @@ def state_arrays(n: int, dt16, device, spread: bool = True):
     m, v, 16-bit param).  spread: views of one pool, placed by
     zero_state_layout (as far apart as the pool allows; AdamW streams the five
     at once and runs fastest when they lie far apart in HBM).  The pool takes
-    the free device memory, capped at POOL_CAP and leaving POOL_MARGIN free;
-    if it cannot hold the arrays apart, or spread is False, they are separate
-    allocations.  Returns the arrays and a description of the layout."""
+    the free device memory, capped at POOL_CAP when that holds the arrays
+    apart, and leaves POOL_MARGIN free; if it cannot hold the arrays apart,
+    or spread is False, they are separate allocations.  Returns the arrays and a description of the layout."""
     import torch
     import zero_sharded_mixed_grads_amd as z
     sizes = (2 * n, 4 * n, 4 * n, 4 * n, 2 * n)
     dts = (dt16, torch.float32, torch.float32, torch.float32, dt16)
     if spread:
         free, _ = torch.cuda.mem_get_info(device)
-        pool_bytes = min(POOL_CAP, free - POOL_MARGIN) // (2 << 20) * (2 << 20)
-        try:
-            offs = z.zero_state_layout(n, pool_bytes)
-        except z.ZeroError:
-            offs = None
+        most = (free - POOL_MARGIN) // (2 << 20) * (2 << 20)
+        offs = None
+        # a pool of POOL_CAP bytes if it holds the arrays apart, else the
+        # largest one that fits (the 13B shard's 206 GB of state)
+        for pool_bytes in (min(POOL_CAP, most), most):
+            try:
+                offs = z.zero_state_layout(n, pool_bytes)
+                break
+            except z.ZeroError:
+                continue
         pool = None
         if offs is not None:
             try:
@@ -139,6 +150,21 @@ class Workload:
         log(f"[bench] inputs resident in HBM after {time.time() - t0:.1f}s "
             f"({torch.cuda.memory_allocated() / 1e9:.1f} GB allocated)")
 
+    def step_tensors(self, marks=None):
+        """The step read from the per-tensor gradients in place (the rank's
+        per-tensor gradients are final at Nd = 1): statistics, then AdamW,
+        with no gathered shard.  marks: optional one event recorded between
+        the two."""
+        z, cfg = self.z, self.cfg
+        stream = self.torch.cuda.current_stream()
+        s = stream.cuda_stream
+        b, e = z.zero_partition(cfg.psi, cfg.nd, cfg.rank)
+        z.zero_grad_stats_tensors(self.ptrs, self.numels, cfg.dtype, b, e - b,
+                                  cfg.hp.inv_loss_scale, self.fws, self.fws.numel(), self.stats, s)
+        if marks: marks[0].record(stream)
+        z.zero_adam_step_tensors(self.hp, self.ptrs, self.numels, cfg.dtype, b, e - b, self.master,
+                                 self.m, self.v, self.p, cfg.dtype, self.stats, self.state, s)
+
     def step(self, marks=None, fused=True):
         """One pass of the hot path.  fused: gather the rank's gradients and
         compute their statistics in one pass (the rank's per-tensor gradients
@@ -171,16 +197,25 @@ class Workload:
                          cfg.dtype, self.n, self.stats, self.state, s)
 
 
+def _host_bits(t, np_dt):
+    """A host copy of a device tensor's bits, viewed as np_dt (numpy has no
+    bfloat16, so 16-bit tensors travel as int16)."""
+    import torch
+    if t.element_size() == 2:
+        t = t.view(torch.int16)
+    return t.cpu().numpy().view(np_dt).copy()
+
+
 def cpu_baseline(w, target_s: float = 12.0):
     """The oracle, as it is, on a bounded contiguous sample of the same shard
     (copied to host memory): grad stats + AdamW.  The sample is sized for
-    about target_s seconds of work (capped at the whole shard) and repeated
-    until target_s seconds have passed."""
+    about target_s seconds of work, capped at the whole shard and at
+    CPU_SAMPLE_CAP elements, and repeated until target_s seconds have passed."""
     import oracle
     cfg = w.cfg
 
     def host(t, k, np_dt):
-        return t[:k].cpu().numpy().view(np_dt).copy()
+        return _host_bits(t[:k], np_dt)
 
     def once(gb, th, m, v, p):
         t0 = time.perf_counter()
@@ -195,7 +230,7 @@ def cpu_baseline(w, target_s: float = 12.0):
 
     k = min(w.n, 1 << 22)
     dt = once(*arrays(k))
-    k = int(min(w.n, max(k, k * target_s / max(dt, 1e-6))))
+    k = int(min(w.n, CPU_SAMPLE_CAP, max(k, k * target_s / max(dt, 1e-6))))
     a = arrays(k)
     total, reps = 0.0, 0
     while total < target_s:
@@ -237,7 +272,7 @@ def cpu_baseline_one_thread(w, k: int = 1 << 24, target_s: float = 4.0):
     k = min(k, w.n)
 
     def host(t, np_dt):
-        return t[:k].cpu().numpy().view(np_dt).copy()
+        return _host_bits(t[:k], np_dt)
 
     with tempfile.TemporaryDirectory() as d:
         path = os.path.join(d, "sample.npz")
@@ -258,15 +293,60 @@ def cpu_baseline_one_thread(w, k: int = 1 << 24, target_s: float = 4.0):
             "host_cpu": cpu, "host_mem_gb": round(mem_kb / 1e6, 1)}
 
 
-def load_traffic(n_params: int):
-    """HBM bytes per Adam launch from the committed rocprofv3 counter runs,
-    or None if the kernel source changed since they were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"adamw_stream_{workload}_traffic.json")
+
+
+def load_traffic(workload: str, n_params: int):
+    """HBM bytes per AdamW launch on this workload from the committed
+    rocprofv3 counter runs, or None if there are none for it or the kernel
+    source changed since they were taken."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
         return None
-    d = json.load(open(TRAFFIC_FILE))
+    d = json.load(open(path))
     if d.get("kernel_source_sha256_16") != kernel_source_hash() or d.get("n") != n_params:
         return None
     return d.get("bytes_per_launch")
+
+
+def time_tensor_step(w, steps: int, warmup: int):
+    """Times `steps` passes of the 30 B/param step (statistics read in place,
+    then AdamW reading the per-tensor gradients) on the same workload, after
+    `warmup` untimed ones; every step must be a real update."""
+    import torch
+    taken0 = w.z.read_adam_state(w.state).step
+    for _ in range(warmup):
+        w.step_tensors()
+    stream = torch.cuda.current_stream()
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    marks = [[torch.cuda.Event(enable_timing=True)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    bounds[0].record(stream)
+    for k in range(steps):
+        w.step_tensors(marks[k])
+        bounds[k + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = w.z.read_adam_state(w.state)
+    if st.step != taken0 + warmup + steps:
+        raise SystemExit("bench: a step of the in-place step was skipped; timing invalid")
+    ms = np.array([[bounds[k].elapsed_time(marks[k][0]), marks[k][0].elapsed_time(bounds[k + 1])]
+                   for k in range(steps)])
+    stats_ms, adam_ms = ms.mean(axis=0)
+    step_ms = wall * 1e3 / steps
+    n = w.n
+    log(f"[bench] in-place step: {step_ms:.3f} ms/step (stats {stats_ms:.3f} ms, "
+        f"adam {adam_ms:.3f} ms)")
+    return {"steps": steps, "ms_per_step": step_ms, "params_per_s": n / (step_ms * 1e-3),
+            "bytes_per_param": ADAM_BYTES_PER_PARAM + STATS_BYTES_PER_PARAM,
+            "kernels": {"grad_stats_tensors": {"ms": stats_ms,
+                                               "GB/s": STATS_BYTES_PER_PARAM * n / stats_ms / 1e6},
+                        "adam_step_tensors": {"ms": adam_ms,
+                                              "GB/s": ADAM_BYTES_PER_PARAM * n / adam_ms / 1e6,
+                                              "frac": ADAM_BYTES_PER_PARAM * n / adam_ms / 1e6
+                                              / HBM_PEAK_GBS}}}
 
 
 def copy_ceiling(device, reps: int = 20):
@@ -607,7 +687,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", type=int, default=4,
+                    help="workload: 4 = 13B list at Nd 1 (default), 2 = GPT-2 1.5B list at Nd 1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time plain device copies of a known size instead")
@@ -707,7 +788,8 @@ def main():
             "bytes_per_param": STATS_BYTES_PER_PARAM}
         step_bytes = ADAM_BYTES_PER_PARAM + STATS_BYTES_PER_PARAM + FLATTEN_BYTES_PER_PARAM
     adam_gbs = ADAM_BYTES_PER_PARAM * n / (adam_ms * 1e-3) / 1e9
-    traffic = load_traffic(n)
+    workload = w.cfg.name + f"-nd{w.cfg.nd}-rank{w.cfg.rank}"
+    traffic = load_traffic(workload, n)
     out = {
         "metric": METRIC,
         "value": n / (step_ms * 1e-3),
@@ -721,7 +803,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.cfg.name + f"-nd{w.cfg.nd}-rank{w.cfg.rank}", "psi": w.cfg.psi,
+        "config": {"workload": workload, "psi": w.cfg.psi,
                    "nd": w.cfg.nd, "rank": w.cfg.rank, "shard_params": n,
                    "grad_dtype": w.cfg.dtype, "param_dtype": w.cfg.dtype,
                    "bucket_elems": w.cfg.bucket_elems, "max_grad_norm": w.cfg.hp.max_grad_norm,
@@ -733,6 +815,8 @@ def main():
         "checks": {"device_steps_taken": int(st.step), "overflow": int(gs.overflow),
                    "sq_norm": gs.sq_norm, "clip_coef": st.coef},
     }
+    # the step read from the per-tensor gradients in place, timed the same way
+    out["step_tensors"] = time_tensor_step(w, min(args.steps, 20), args.warmup)
     # the same process's copy ceiling, for the fraction of what a plain copy reaches
     cc = copy_ceiling(dev)
     if cc is not None:

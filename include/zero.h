@@ -246,34 +246,41 @@ typedef struct {
 
 /* Device-resident step state (64 bytes, 8-byte aligned).  The caller
  * zero-initialises it once; zero_adam_step then advances `step` and fills the
- * per-step scalars (rounded once from fp64) that its element kernel reads. */
+ * per-step fp64 scalars that its element kernel reads. */
 typedef struct {
     uint64_t step;     /* number of steps taken (not advanced by skipped steps) */
     uint32_t skip;     /* 1 if the last call skipped (overflow) */
     uint32_t pad0;
     double coef;       /* clip coefficient of the last step */
-    float grad_mult;   /* inv_loss_scale * coef */
-    float step_size;   /* lr / (1 - beta1^t) */
-    float inv_sqrt_bc2; /* 1 / sqrt(1 - beta2^t) */
-    float beta1, one_minus_beta1, beta2, one_minus_beta2, eps;
-    float decay;       /* lr * weight_decay */
-    uint32_t pad1;
+    double inv_scale;  /* inverse loss scale the last step unscaled its gradients by */
+    double bc1;        /* 1 - beta1^t of the last step */
+    double bc2;        /* 1 - beta2^t of the last step */
+    double inv_bc1;    /* 1 / bc1, correctly rounded */
+    double inv_bc2;    /* 1 / bc2, correctly rounded */
 } zero_adam_state_t;
 
 /* [P2] ZeRO-DP Stage 1/2: each rank updates only its own part of the
  * optimizer state, once, at the end of the step ([P2] 考察); [P2] memory
  * accounting fixes the arrays: 16-bit params and grads, fp32 master,
  * momentum and variance; [P4] 显存背景 names the optimizer AdamW.
- * For every element i < n of the shard:
- *   g  = grad[i] * inv * coef
- *   m  = beta1 m + (1 - beta1) g;   v = beta2 v + (1 - beta2) g^2
- *   master = master - lr wd master - lr (m / (1 - beta1^t)) /
- *            (sqrt(v / (1 - beta2^t)) + eps)
- *   param_out[i] = master rounded to pdt (nearest, ties to even)
+ * For every element i < n of the shard, in fp64 arithmetic on the stored
+ * values, in this order:
+ *   g  = (grad[i] * inv) * coef
+ *   m  = beta1 m + (1 - beta1) g;   v = beta2 v + ((1 - beta2) g) g
+ *   master = (master - (lr wd) master) -
+ *            (lr (m / bc1)) / (sqrt(v / bc2) + eps)
+ * with bc1 = 1 - beta1^t and bc2 = 1 - beta2^t (the two quotients by them
+ * are formed from their correctly rounded reciprocals with one fused
+ * correction, which gives the correctly rounded quotient: Markstein's
+ * theorem); m, v and master are then stored rounded once to fp32 (nearest,
+ * ties to even), and
+ *   param_out[i] = the stored fp32 master rounded to pdt (nearest, ties to even)
  * with t the advanced step count, coef = min(1, max_grad_norm / ||g||)
  * (1 when clipping is off or d_stats is NULL), computed in fp64 on the
  * device from *d_stats, and inv = d_scale->inv_scale (read on the device)
- * when d_scale is not NULL, else hp->inv_loss_scale.  With dynamic loss
+ * when d_scale is not NULL, else hp->inv_loss_scale.  Every operation is
+ * an IEEE fp64 operation, correctly rounded, none fused, so the results are
+ * those of evaluating the lines above in fp64 as written.  With dynamic loss
  * scaling, call zero_loss_scale_update after this call, on the same stream,
  * so that the step uses the scale its gradients were computed with.  If
  * d_stats reports overflow, the step is skipped: nothing is written to the
@@ -282,8 +289,8 @@ typedef struct {
  * updated in place; param_out: n 16-bit params (pdt), written.  d_stats:
  * device result of zero_grad_stats (or NULL: no clipping, never skip);
  * d_state: device step state.  n == 0 still advances d_state.
- * Occupancy: every block of the update reserves 64 KiB of LDS that it does
- * not use, so that at most two blocks run per CU (of gfx950's 160 KiB);
+ * Occupancy: every block of the update reserves 48 KiB of LDS that it does
+ * not use, so that at most three blocks run per CU (of gfx950's 160 KiB);
  * kernels that run beside it on other streams share the remaining LDS.
  * Errors: ZERO_EINVAL (NULL hp or d_state, NULL arrays with n > 0, bad
  * dtypes, lr < 0, beta outside [0, 1), eps <= 0, weight_decay < 0, no
@@ -294,6 +301,48 @@ zero_status zero_adam_step(const zero_adamw *hp, const void *grad, zero_dtype gd
                            uint64_t n, const zero_grad_stats_t *d_stats,
                            const zero_loss_scale_t *d_scale, zero_adam_state_t *d_state,
                            void *stream);
+
+/* ---------------------------------------- the step read from tensor lists
+ * For a rank whose per-tensor gradient buffers already hold its final
+ * gradients (one data-parallel rank, or gradients reduced in place), the
+ * gathered flat gradient shard is written only to be read back.  [P2] ZeRO-R,
+ * CB: the fused buffers bound temporary memory; these two calls need none,
+ * and the step moves 30 bytes per parameter (statistics 2 + AdamW 28)
+ * instead of 32 (gather with statistics 4 + AdamW 28). */
+
+/* zero_grad_stats over elements [range_begin, range_begin + count) of the
+ * list-order flat stream of the 16-bit gradient tensors (described as for
+ * zero_bucket_flatten), read in place: nothing is written but *d_stats.  The
+ * result equals, bit for bit, what zero_bucket_flatten_stats writes for the
+ * same range into a 16-byte aligned dst.  workspace: at least
+ * zero_bucket_flatten_stats_workspace(numel, n_tensors, range_begin, count)
+ * bytes, 16-byte aligned.  count == 0 writes {0, 0}.  Errors: as
+ * zero_bucket_flatten_stats (ZERO_EINVAL, ZERO_ENOSPC, ZERO_EALIGN,
+ * ZERO_EDEVICE); the tensors must not overlap workspace, d_stats or d_scale. */
+zero_status zero_grad_stats_tensors(const void *const *tensor_ptrs, const uint64_t *numel,
+                                    uint32_t n_tensors, zero_dtype gdt, uint64_t range_begin,
+                                    uint64_t count, double inv_loss_scale,
+                                    const zero_loss_scale_t *d_scale, void *workspace,
+                                    size_t ws_bytes, zero_grad_stats_t *d_stats, void *stream);
+
+/* zero_adam_step with its gradients read in place from the tensors: element i
+ * (i < count) of master, exp_avg, exp_avg_sq and param_out is updated with
+ * the gradient at position range_begin + i of the tensors' list-order flat
+ * stream (tensors described as for zero_bucket_flatten, gdt F16 or BF16).
+ * The arithmetic, the step state, clipping, skipping and every result are
+ * those of zero_adam_step on the gathered gradients, bit for bit.  master,
+ * exp_avg and exp_avg_sq must lie at the same position within 16 bytes
+ * (ZERO_EALIGN otherwise); param_out may lie anywhere 2-byte aligned.
+ * count == 0 still advances d_state.  The tensors must not overlap any
+ * output.  Errors: as zero_adam_step and zero_bucket_flatten (ZERO_EINVAL,
+ * ZERO_EALIGN, ZERO_EDEVICE); arguments are checked before anything runs. */
+zero_status zero_adam_step_tensors(const zero_adamw *hp, const void *const *tensor_ptrs,
+                                   const uint64_t *numel, uint32_t n_tensors, zero_dtype gdt,
+                                   uint64_t range_begin, uint64_t count, float *master,
+                                   float *exp_avg, float *exp_avg_sq, void *param_out,
+                                   zero_dtype pdt, const zero_grad_stats_t *d_stats,
+                                   const zero_loss_scale_t *d_scale, zero_adam_state_t *d_state,
+                                   void *stream);
 
 /* Sets *d_scale (device) to {cfg->init_scale, 1 / init_scale, 0, 0} with a
  * one-thread kernel, ordered on `stream`.  Errors: ZERO_EINVAL (NULL

@@ -47,7 +47,7 @@ def test_ckpt_roundtrip_and_reshard(tmp_path):
                 assert np.array_equal(got.cpu().numpy().view(np.uint32),
                                       ref[b:e].view(np.uint32)), (nd_new, r)
             s = z.read_adam_state(st)
-            assert s.step == 17 and s.skip == 0 and s.grad_mult == 0.0
+            assert s.step == 17 and s.skip == 0 and s.bc1 == 0.0 and s.bc2 == 0.0
 
 
 def _train(bufs, p, grads, hp, state, stats_mode):

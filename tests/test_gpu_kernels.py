@@ -191,7 +191,7 @@ def test_adam_one_step_dtypes_sizes(gdt, pdt, n):
     s, th, m, v, p = _oracle_step(c, hp, gdt, pdt, True, st.sq_norm, st.overflow)
     e = check_adam_one_step(hp, s, oracle.value16(c["gb"], gdt), c["th0"], c["m0"],
                             c["v0"], c["th"].host(), c["m"].host(), c["v"].host(), th, m, v)
-    check_params16(c["p"].host(), c["th"].host(), th, e["master_scale"], 1e-6, pdt)
+    check_params16(c["p"].host(), c["th"].host(), th, pdt)
     sa = z.read_adam_state(c["state"])
     assert sa.step == 1 and sa.skip == 0 and abs(sa.coef - s.coef) <= 1e-12
     for b in ("g", "th", "m", "v", "p"):
@@ -208,7 +208,7 @@ def test_adam_16bit_phases(g_phase, p_phase):
     s, th, m, v, p = _oracle_step(c, hp, "f16", "f16", True, st.sq_norm, st.overflow)
     e = check_adam_one_step(hp, s, oracle.value16(c["gb"], "f16"), c["th0"], c["m0"],
                             c["v0"], c["th"].host(), c["m"].host(), c["v"].host(), th, m, v)
-    check_params16(c["p"].host(), c["th"].host(), th, e["master_scale"], 1e-6, "f16")
+    check_params16(c["p"].host(), c["th"].host(), th, "f16")
     for b in ("g", "th", "m", "v", "p"):
         assert c[b].canaries_intact(), b
 
@@ -223,7 +223,7 @@ def test_adam_fp32_phases_and_fallback(f_phases):
         s, th, m, v, p = _oracle_step(c, hp, "bf16", "bf16", True, st.sq_norm, st.overflow)
         e = check_adam_one_step(hp, s, oracle.value16(c["gb"], "bf16"), c["th0"], c["m0"],
                                 c["v0"], c["th"].host(), c["m"].host(), c["v"].host(), th, m, v)
-        check_params16(c["p"].host(), c["th"].host(), th, e["master_scale"], 1e-6, "bf16")
+        check_params16(c["p"].host(), c["th"].host(), th, "bf16")
         for b in ("g", "th", "m", "v", "p"):
             assert c[b].canaries_intact(), b
 
@@ -274,7 +274,7 @@ def test_adam_degenerate_hyperparameters(case):
     e = check_adam_one_step(hp, s, oracle.value16(c["gb"], "bf16"), c["th0"], c["m0"],
                             c["v0"], c["th"].host(), c["m"].host(), c["v"].host(), th, m, v,
                             label=case)
-    check_params16(c["p"].host(), c["th"].host(), th, e["master_scale"], 1e-6, "f16")
+    check_params16(c["p"].host(), c["th"].host(), th, "f16")
     if case == "lr_0":
         assert np.array_equal(c["th"].host(), c["th0"] + np.float32(0.0))
     sa = z.read_adam_state(c["state"])

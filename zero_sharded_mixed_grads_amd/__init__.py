@@ -48,11 +48,8 @@ class GradStats(ctypes.Structure):  # zero_grad_stats_t, device resident
 
 class AdamState(ctypes.Structure):  # zero_adam_state_t, device resident
     _fields_ = [("step", U64), ("skip", U32), ("pad0", U32), ("coef", DBL),
-                ("grad_mult", ctypes.c_float), ("step_size", ctypes.c_float),
-                ("inv_sqrt_bc2", ctypes.c_float), ("beta1", ctypes.c_float),
-                ("one_minus_beta1", ctypes.c_float), ("beta2", ctypes.c_float),
-                ("one_minus_beta2", ctypes.c_float), ("eps", ctypes.c_float),
-                ("decay", ctypes.c_float), ("pad1", U32)]
+                ("inv_scale", DBL), ("bc1", DBL), ("bc2", DBL), ("inv_bc1", DBL),
+                ("inv_bc2", DBL)]
 
 
 class LossScaler(ctypes.Structure):  # zero_loss_scaler, host parameters
@@ -77,6 +74,7 @@ assert ctypes.sizeof(LossScaler) == 48 and ctypes.sizeof(LossScale) == 32
 EXPORTS = ("zero_status_str", "zero_last_error", "zero_partition", "zero_mem_bytes",
            "zero_bucket_plan", "zero_bucket_flatten", "zero_grad_stats_workspace",
            "zero_grad_stats", "zero_bucket_flatten_stats_workspace", "zero_bucket_flatten_stats",
+           "zero_grad_stats_tensors", "zero_adam_step_tensors",
            "zero_adam_step", "zero_offload_staging_bytes", "zero_offload_adam_step",
            "zero_ckpt_save", "zero_ckpt_read_header", "zero_ckpt_load",
            "zero_loss_scale_init", "zero_loss_scale_update", "zero_state_layout")
@@ -88,45 +86,56 @@ def lib():
     """The loaded library (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: build it with "
-                              "`python -c 'import __graft_entry__ as g; g.build()'`")
-        L = ctypes.CDLL(LIB_PATH)
-        L.zero_status_str.argtypes = [ctypes.c_int]
-        L.zero_status_str.restype = ctypes.c_char_p
-        L.zero_last_error.argtypes = []
-        L.zero_last_error.restype = ctypes.c_char_p
-        L.zero_partition.argtypes = [U64, U32, U32, ctypes.POINTER(U64), ctypes.POINTER(U64)]
-        L.zero_mem_bytes.argtypes = [U32, U64, U32, U32, ctypes.POINTER(U64)]
-        L.zero_bucket_plan.argtypes = [ctypes.POINTER(U64), U32, U64, U64, U64,
-                                       ctypes.POINTER(Segment), U64, ctypes.POINTER(U64)]
-        L.zero_bucket_flatten.argtypes = [ctypes.POINTER(VP), ctypes.POINTER(U64), U32,
-                                          ctypes.c_int, U64, U64, VP, VP]
-        L.zero_grad_stats_workspace.argtypes = [U64, ctypes.POINTER(ctypes.c_size_t)]
-        L.zero_grad_stats.argtypes = [VP, ctypes.c_int, U64, DBL, VP, VP, ctypes.c_size_t, VP,
-                                      VP]
-        L.zero_bucket_flatten_stats_workspace.argtypes = [ctypes.POINTER(U64), U32, U64, U64,
-                                                          ctypes.POINTER(ctypes.c_size_t)]
-        L.zero_bucket_flatten_stats.argtypes = [ctypes.POINTER(VP), ctypes.POINTER(U64), U32,
-                                                ctypes.c_int, U64, U64, VP, DBL, VP, VP,
-                                                ctypes.c_size_t, VP, VP]
-        L.zero_adam_step.argtypes = [ctypes.POINTER(AdamW), VP, ctypes.c_int, VP, VP, VP, VP,
-                                     ctypes.c_int, U64, VP, VP, VP, VP]
-        L.zero_loss_scale_init.argtypes = [ctypes.POINTER(LossScaler), VP, VP]
-        L.zero_state_layout.argtypes = [U64, U64, ctypes.POINTER(U64)]
-        L.zero_loss_scale_update.argtypes = [ctypes.POINTER(LossScaler), VP, VP, VP]
-        L.zero_offload_staging_bytes.argtypes = [U64, ctypes.POINTER(ctypes.c_size_t)]
-        L.zero_offload_adam_step.argtypes = [ctypes.POINTER(AdamW), VP, ctypes.c_int, VP, VP,
-                                             VP, VP, ctypes.c_int, U64, VP, VP, VP, VP,
-                                             ctypes.c_size_t, VP]
-        L.zero_ckpt_save.argtypes = [ctypes.c_char_p, U64, U32, U32, VP, VP, VP, VP, VP, VP]
-        L.zero_ckpt_read_header.argtypes = [ctypes.c_char_p, ctypes.POINTER(CkptHeader)]
-        L.zero_ckpt_load.argtypes = [ctypes.POINTER(ctypes.c_char_p), U32, U64, U32, U32, VP, VP,
-                                     VP, VP, VP, VP]
-        for name in EXPORTS[2:]:
-            getattr(L, name).restype = ctypes.c_int
-        _lib = L
+        _lib = load(LIB_PATH)
     return _lib
+
+
+def load(path: str):
+    """Loads a build of the library at `path` and declares its signatures."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(path)
+    L.zero_status_str.argtypes = [ctypes.c_int]
+    L.zero_status_str.restype = ctypes.c_char_p
+    L.zero_last_error.argtypes = []
+    L.zero_last_error.restype = ctypes.c_char_p
+    L.zero_partition.argtypes = [U64, U32, U32, ctypes.POINTER(U64), ctypes.POINTER(U64)]
+    L.zero_mem_bytes.argtypes = [U32, U64, U32, U32, ctypes.POINTER(U64)]
+    L.zero_bucket_plan.argtypes = [ctypes.POINTER(U64), U32, U64, U64, U64,
+                                   ctypes.POINTER(Segment), U64, ctypes.POINTER(U64)]
+    L.zero_bucket_flatten.argtypes = [ctypes.POINTER(VP), ctypes.POINTER(U64), U32,
+                                      ctypes.c_int, U64, U64, VP, VP]
+    L.zero_grad_stats_workspace.argtypes = [U64, ctypes.POINTER(ctypes.c_size_t)]
+    L.zero_grad_stats.argtypes = [VP, ctypes.c_int, U64, DBL, VP, VP, ctypes.c_size_t, VP,
+                                  VP]
+    L.zero_grad_stats_tensors.argtypes = [ctypes.POINTER(VP), ctypes.POINTER(U64), U32,
+                                          ctypes.c_int, U64, U64, DBL, VP, VP, ctypes.c_size_t,
+                                          VP, VP]
+    L.zero_adam_step_tensors.argtypes = [ctypes.POINTER(AdamW), ctypes.POINTER(VP),
+                                         ctypes.POINTER(U64), U32, ctypes.c_int, U64, U64, VP,
+                                         VP, VP, VP, ctypes.c_int, VP, VP, VP, VP]
+    L.zero_bucket_flatten_stats_workspace.argtypes = [ctypes.POINTER(U64), U32, U64, U64,
+                                                      ctypes.POINTER(ctypes.c_size_t)]
+    L.zero_bucket_flatten_stats.argtypes = [ctypes.POINTER(VP), ctypes.POINTER(U64), U32,
+                                            ctypes.c_int, U64, U64, VP, DBL, VP, VP,
+                                            ctypes.c_size_t, VP, VP]
+    L.zero_adam_step.argtypes = [ctypes.POINTER(AdamW), VP, ctypes.c_int, VP, VP, VP, VP,
+                                 ctypes.c_int, U64, VP, VP, VP, VP]
+    L.zero_loss_scale_init.argtypes = [ctypes.POINTER(LossScaler), VP, VP]
+    L.zero_state_layout.argtypes = [U64, U64, ctypes.POINTER(U64)]
+    L.zero_loss_scale_update.argtypes = [ctypes.POINTER(LossScaler), VP, VP, VP]
+    L.zero_offload_staging_bytes.argtypes = [U64, ctypes.POINTER(ctypes.c_size_t)]
+    L.zero_offload_adam_step.argtypes = [ctypes.POINTER(AdamW), VP, ctypes.c_int, VP, VP,
+                                         VP, VP, ctypes.c_int, U64, VP, VP, VP, VP,
+                                         ctypes.c_size_t, VP]
+    L.zero_ckpt_save.argtypes = [ctypes.c_char_p, U64, U32, U32, VP, VP, VP, VP, VP, VP]
+    L.zero_ckpt_read_header.argtypes = [ctypes.c_char_p, ctypes.POINTER(CkptHeader)]
+    L.zero_ckpt_load.argtypes = [ctypes.POINTER(ctypes.c_char_p), U32, U64, U32, U32, VP, VP,
+                                 VP, VP, VP, VP]
+    for name in EXPORTS[2:]:
+        getattr(L, name).restype = ctypes.c_int
+    return L
 
 
 def _check(status: int):
@@ -266,6 +275,29 @@ def zero_adam_step(hp: AdamW, grad, gdtype, master, exp_avg, exp_avg_sq, param_o
                                 _ptr(exp_avg), _ptr(exp_avg_sq), _ptr(param_out), _dtype(pdtype),
                                 n, _ptr(d_stats), _ptr(d_scale), _ptr(d_state),
                                 _stream(stream)))
+
+
+def zero_grad_stats_tensors(tensors: Sequence, numel: Optional[Sequence[int]], gdtype,
+                            range_begin: int, count: int, inv_loss_scale: float, workspace,
+                            ws_bytes: int, d_stats, stream=None, d_scale=None) -> None:
+    """tensors and numel as for zero_bucket_flatten; the gradients are read in
+    place (workspace from zero_bucket_flatten_stats_workspace)."""
+    ptrs, nums = tensor_table(tensors, numel)
+    _check(lib().zero_grad_stats_tensors(ptrs, nums, len(ptrs), _dtype(gdtype), range_begin,
+                                         count, inv_loss_scale, _ptr(d_scale), _ptr(workspace),
+                                         ws_bytes, _ptr(d_stats), _stream(stream)))
+
+
+def zero_adam_step_tensors(hp: AdamW, tensors: Sequence, numel: Optional[Sequence[int]], gdtype,
+                           range_begin: int, count: int, master, exp_avg, exp_avg_sq, param_out,
+                           pdtype, d_stats, d_state, stream=None, d_scale=None) -> None:
+    """zero_adam_step with the gradients read in place from the tensors."""
+    ptrs, nums = tensor_table(tensors, numel)
+    _check(lib().zero_adam_step_tensors(ctypes.byref(hp), ptrs, nums, len(ptrs), _dtype(gdtype),
+                                        range_begin, count, _ptr(master), _ptr(exp_avg),
+                                        _ptr(exp_avg_sq), _ptr(param_out), _dtype(pdtype),
+                                        _ptr(d_stats), _ptr(d_scale), _ptr(d_state),
+                                        _stream(stream)))
 
 
 def zero_loss_scale_init(cfg: LossScaler, d_scale, stream=None) -> None:

@@ -1,8 +1,13 @@
 """Builds libzero_mi355x.so in-tree with hipcc for gfx950.
 
-Two translation units: the host planner (C++) and the HIP device path.
-All HIP code is compiled without packed-fp32 instructions and without
-denormal flushing.
+Translation units: the host planner, checkpoint and offload code (C++) and
+the HIP device path.  All HIP code is compiled without packed-fp32
+instructions and without denormal flushing.
+
+A second library, libzero_mi355x_capped.so, is the same code with the
+per-launch block cap lowered to 64 blocks, so that tests reach the
+multi-launch and multi-round paths (taken above about 17e9 elements with
+the real cap) on small inputs.
 """
 import os
 import subprocess
@@ -13,6 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libzero_mi355x.so")
+CAPPED_LIB = os.path.join(PKG, "libzero_mi355x_capped.so")
+CAPPED_BLOCKS = 64
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -37,8 +44,14 @@ def _run(cmd):
     subprocess.check_call(cmd)
 
 
+def _link(objs, out):
+    tmp = out + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, *LINK, "-o", tmp])
+    os.replace(tmp, out)
+
+
 def build(verbose: bool = True) -> str:
-    """Compile every source and link the shared library (always rebuilds)."""
+    """Compile every source and link both libraries (always rebuilds)."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     objs = []
     for src in SOURCES:
@@ -50,9 +63,15 @@ def build(verbose: bool = True) -> str:
             _run([HIPCC, *COMMON, *HOST, *EXTRA.get(src, []), "-x", "c++", "-c", path, "-o",
                   obj])
         objs.append(obj)
-    tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, *LINK, "-o", tmp])
-    os.replace(tmp, LIB)
+    _link(objs, LIB)
+    capped = []
+    for src, obj in zip(SOURCES, objs):
+        if src.endswith(".hip"):
+            obj = os.path.join(BUILD_DIR, src + ".capped.o")
+            _run([HIPCC, *COMMON, *DEVICE, f"-DZERO_MAX_LAUNCH_BLOCKS={CAPPED_BLOCKS}", "-x",
+                  "hip", "-c", os.path.join(CSRC, src), "-o", obj])
+        capped.append(obj)
+    _link(capped, CAPPED_LIB)
     return LIB
 
 

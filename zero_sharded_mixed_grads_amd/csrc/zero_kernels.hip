@@ -69,6 +69,25 @@ __device__ __forceinline__ void st_stream(T *p, const T &v)
     *p = v;
 }
 
+// A load through a pointer that the compiler cannot prove global (a tensor
+// address read from a table), issued as a global load: a flat load would
+// also count against the scalar-memory counter, so every later scalar load
+// (the next tile's table lookup) would wait for it.
+template <typename T>
+__device__ __forceinline__ T ld_global(const T *p)
+{
+    return *(const __attribute__((address_space(1))) T *)p;
+}
+
+// (uint4's copy constructor would take a generic reference: load a native
+// vector instead.)
+__device__ __forceinline__ uint4 ld_global(const uint4 *p)
+{
+    typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+    const v4u32 x = *(const __attribute__((address_space(1))) v4u32 *)p;
+    return make_uint4(x.x, x.y, x.z, x.w);
+}
+
 // ------------------------------------------------------------ 16-bit helpers
 template <bool BF16>
 __device__ __forceinline__ float to_f32(uint32_t h)  // h: bits in the low half
@@ -303,6 +322,16 @@ __device__ __forceinline__ uint32_t count_le(const uint32_t *c, uint32_t t)
     return N - above;
 }
 
+// Segment of tile `tile`: the largest s with tile_lo[s] <= tile (uniform).
+// tile_lo rises strictly from tile_lo[0] = 0 and then reads values above
+// every tile, so s + 1 is the count of entries <= tile: found as a count
+// among the coarse entries, then among the chosen slot's fine entries.
+__device__ __forceinline__ uint32_t find_segment(const FlatArgs &a, uint32_t tile)
+{
+    const uint32_t j = count_le<kSegCoarse>(a.coarse, tile) - 1;
+    return j * kSegFan + count_le<kSegFan>(a.tile_lo + j * kSegFan, tile) - 1;
+}
+
 template <bool BF16>
 __device__ __forceinline__ void accum2(uint32_t w, double &acc)
 {
@@ -341,9 +370,9 @@ __device__ __forceinline__ void flatten_full_chunks(const char *src_line0, char 
         const uint64_t c = c_beg + (uint64_t)j * kBlock + threadIdx.x;
         if (c < c_end) {
             const uint4 *s = reinterpret_cast<const uint4 *>(src_line0) + c;
-            lo[j] = s[0];
+            lo[j] = ld_global(s);
             if constexpr (SB != 0)
-                hi[j] = s[1];
+                hi[j] = ld_global(s + 1);
         }
     }
 #pragma unroll
@@ -357,10 +386,11 @@ __device__ __forceinline__ void flatten_full_chunks(const char *src_line0, char 
                 o = shift_lines<SB>(lo[j], hi[j]);
             reinterpret_cast<uint4 *>(dst_line0)[c] = o;
             if constexpr (MODE != kCopy) {
-                accum2<MODE == kStatsBF16>(o.x, acc);
-                accum2<MODE == kStatsBF16>(o.y, acc);
-                accum2<MODE == kStatsBF16>(o.z, acc);
-                accum2<MODE == kStatsBF16>(o.w, acc);
+                constexpr bool bf = MODE == kStatsBF16;
+                accum2<bf>(o.x, acc);
+                accum2<bf>(o.y, acc);
+                accum2<bf>(o.z, acc);
+                accum2<bf>(o.w, acc);
             }
         }
     }
@@ -371,12 +401,7 @@ __global__ void __launch_bounds__(kBlock) flatten_segments(FlatArgs a)
 {
     constexpr uint64_t V = 16 / ES;  // elements per 16-byte line
     const uint32_t tile = blockIdx.x;  // one tile per block: the grid is the tile count
-    // segment of this tile: the largest s with tile_lo[s] <= tile (uniform).
-    // tile_lo rises strictly from tile_lo[0] = 0 and then reads values above
-    // every tile, so s + 1 is the count of entries <= tile: found as a count
-    // among the coarse entries, then among the chosen slot's fine entries.
-    const uint32_t j = count_le<kSegCoarse>(a.coarse, tile) - 1;
-    const uint32_t s = j * kSegFan + count_le<kSegFan>(a.tile_lo + j * kSegFan, tile) - 1;
+    const uint32_t s = find_segment(a, tile);
     const uint64_t e_lo = a.seg_lo[s], e_hi = a.seg_lo[s + 1];
     const uint64_t ph = a.dst_phase;
     // full destination lines inside the segment: [c0, c1) in line units
@@ -394,7 +419,7 @@ __global__ void __launch_bounds__(kBlock) flatten_segments(FlatArgs a)
         if (i < n_head + n_tail) {
             const uint64_t e = i < n_head ? e_lo + i : tail_beg + (i - n_head);
             if constexpr (ES == 2) {
-                const uint16_t v = reinterpret_cast<const uint16_t *>(src)[e - e_lo];
+                const uint16_t v = ld_global(reinterpret_cast<const uint16_t *>(src) + (e - e_lo));
                 reinterpret_cast<uint16_t *>(a.dst)[e] = v;
                 if constexpr (MODE != kCopy) {
                     const double x = (double)to_f32<MODE == kStatsBF16>(v);
@@ -402,7 +427,7 @@ __global__ void __launch_bounds__(kBlock) flatten_segments(FlatArgs a)
                 }
             } else {
                 reinterpret_cast<uint32_t *>(a.dst)[e] =
-                    reinterpret_cast<const uint32_t *>(src)[e - e_lo];
+                    ld_global(reinterpret_cast<const uint32_t *>(src) + (e - e_lo));
             }
         }
     }
@@ -439,6 +464,86 @@ __global__ void __launch_bounds__(kBlock) flatten_segments(FlatArgs a)
     }
 }
 
+// Statistics of the gather's tiles without the copy: every block takes
+// kStatsTilesPerBlock consecutive tiles and, for each, sums exactly the
+// squares that flatten_segments<2, stats> sums for it, in the same order
+// (the tile's edge elements first, then its thread's line), and leaves the
+// same per-tile partial.  The loads of all its tiles are issued before any is
+// summed, so a block keeps several lines per thread in flight.
+constexpr int kStatsTilesPerBlock = 4;
+
+template <bool BF16>
+__global__ void __launch_bounds__(kBlock) stats_segments(FlatArgs a)
+{
+    constexpr int T = kStatsTilesPerBlock;
+    uint4 lo[T], hi[T];
+    uint32_t sb[T];
+    bool line[T];
+    uint16_t edge[T];
+    bool has_edge[T];
+    // the lines of every tile first, then the edge elements, then the sums
+#pragma unroll
+    for (int q = 0; q < T; ++q) {
+        line[q] = has_edge[q] = false;
+        sb[q] = 0;
+        hi[q] = make_uint4(0, 0, 0, 0);
+        const uint32_t tile = blockIdx.x * T + q;
+        if (tile >= a.n_tiles)
+            continue;
+        const uint32_t s = find_segment(a, tile);
+        const uint64_t e_lo = a.seg_lo[s], e_hi = a.seg_lo[s + 1];
+        const uint64_t ph = a.dst_phase;
+        const uint64_t c0 = (e_lo + ph + 7) / 8, c1 = (e_hi + ph) / 8;
+        const bool has_full = c1 > c0;
+        const uint64_t k = tile - a.tile_lo[s];
+        const uint16_t *src = reinterpret_cast<const uint16_t *>(a.src[s]);
+        if (has_full) {
+            const uint64_t c = k * kFlatTileChunks + threadIdx.x;
+            if (c < c1 - c0) {
+                const uintptr_t s0 = (uintptr_t)(src + (c0 * 8 - ph - e_lo));
+                sb[q] = (uint32_t)(s0 & 15u);
+                const uint4 *sl = reinterpret_cast<const uint4 *>(s0 - sb[q]) + c;
+                lo[q] = ld_global(sl);
+                if (sb[q])
+                    hi[q] = ld_global(sl + 1);
+                line[q] = true;
+            }
+        }
+        if (k == 0) {
+            const uint64_t head_end = has_full ? c0 * 8 - ph : e_hi;
+            const uint64_t tail_beg = has_full ? c1 * 8 - ph : e_hi;
+            const uint64_t n_head = head_end - e_lo, n_tail = e_hi - tail_beg;
+            const uint64_t i = threadIdx.x;
+            if (i < n_head + n_tail) {
+                const uint64_t e = i < n_head ? e_lo + i : tail_beg + (i - n_head);
+                edge[q] = ld_global(src + (e - e_lo));
+                has_edge[q] = true;
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < T; ++q) {
+        double acc = 0.0;
+        if (has_edge[q]) {
+            const double x = (double)to_f32<BF16>(edge[q]);
+            acc = fma(x, x, acc);
+        }
+        if (line[q]) {
+            const uint4 o = sb[q] ? shift_lines_rt(lo[q], hi[q], sb[q]) : lo[q];
+            accum2<BF16>(o.x, acc);
+            accum2<BF16>(o.y, acc);
+            accum2<BF16>(o.z, acc);
+            accum2<BF16>(o.w, acc);
+        }
+        const uint32_t tile = blockIdx.x * T + q;
+        if (tile < a.n_tiles) {  // uniform: every thread of the block takes the barrier
+            const double t = block_sum(acc);
+            if (threadIdx.x == 0)
+                a.part[a.tile_base + tile] = t;
+        }
+    }
+}
+
 // ============================================================ grad stats
 // One tile of kStatsTileLines 16-byte lines (8 gradients each) per block; each
 // tile leaves one fp64 partial sum of squares, and the partials are reduced in
@@ -472,14 +577,15 @@ size_t partials_bytes(uint64_t tiles)
 
 size_t stats_workspace_bytes(uint64_t n) { return partials_bytes(stats_tiles_max(n)); }
 
+// Adds the squares of tile `tile`'s gradients that this thread holds to acc:
+// ZERO_STATS_LINES aligned 16-byte lines per thread, and, in tile 0, the
+// elements outside the aligned lines ([0, head) and [tail_beg, n)).
 template <bool BF16>
-__global__ void __launch_bounds__(kBlock)
-    stats_pass1(const uint16_t *g, uint64_t head, uint64_t nchunks, uint64_t tail_beg, uint64_t n,
-                uint64_t tile0, double *part)
+__device__ __forceinline__ void stats_tile(const uint16_t *g, uint64_t head, uint64_t nchunks,
+                                           uint64_t tail_beg, uint64_t n, uint64_t tile,
+                                           double &acc)
 {
-    double acc = 0.0;
     const uint4 *lines = reinterpret_cast<const uint4 *>(g + head);
-    const uint64_t tile = tile0 + blockIdx.x;
     const uint64_t base = tile * kStatsTileLines + threadIdx.x;
     uint4 w[ZERO_STATS_LINES];
 #pragma unroll
@@ -494,7 +600,7 @@ __global__ void __launch_bounds__(kBlock)
         accum2<BF16>(w[j].z, acc);
         accum2<BF16>(w[j].w, acc);
     }
-    if (tile == 0) {  // elements outside the aligned lines: [0, head) and [tail_beg, n)
+    if (tile == 0) {
         const uint64_t n_edge = head + (n - tail_beg);
         if (threadIdx.x < n_edge) {
             const uint64_t e = threadIdx.x < head ? threadIdx.x : tail_beg + (threadIdx.x - head);
@@ -502,6 +608,17 @@ __global__ void __launch_bounds__(kBlock)
             acc = fma(x, x, acc);
         }
     }
+}
+
+// One tile per block: block b leaves the partial of tile tile0 + b.
+template <bool BF16>
+__global__ void __launch_bounds__(kBlock)
+    stats_pass1(const uint16_t *g, uint64_t head, uint64_t nchunks, uint64_t tail_beg, uint64_t n,
+                uint64_t tile0, double *part)
+{
+    double acc = 0.0;
+    const uint64_t tile = tile0 + blockIdx.x;
+    stats_tile<BF16>(g, head, nchunks, tail_beg, n, tile, acc);
     const double t = block_sum(acc);
     if (threadIdx.x == 0)
         part[tile] = t;
@@ -542,7 +659,7 @@ __global__ void __launch_bounds__(kBlock)
 }
 
 // ================================================================= AdamW
-// Per-step scalars, computed once in fp64 by one thread and rounded once.
+// Per-step scalars, computed once in fp64 by one thread.
 __global__ void adam_scalars(zero_adamw hp, const zero_grad_stats_t *stats,
                              const zero_loss_scale_t *scale, zero_adam_state_t *st)
 {
@@ -563,21 +680,16 @@ __global__ void adam_scalars(zero_adamw hp, const zero_grad_stats_t *stats,
                 coef = hp.max_grad_norm / norm;
         }
     }
-    const double bc1 = 1.0 - pow(hp.beta1, (double)t);
-    const double bc2 = 1.0 - pow(hp.beta2, (double)t);
     st->step = t;
     st->skip = 0;
     st->coef = coef;
-    const double inv = scale ? scale->inv_scale : hp.inv_loss_scale;
-    st->grad_mult = (float)(inv * coef);
-    st->step_size = (float)(hp.lr / bc1);
-    st->inv_sqrt_bc2 = (float)(1.0 / sqrt(bc2));
-    st->beta1 = (float)hp.beta1;
-    st->one_minus_beta1 = (float)(1.0 - hp.beta1);
-    st->beta2 = (float)hp.beta2;
-    st->one_minus_beta2 = (float)(1.0 - hp.beta2);
-    st->eps = (float)hp.eps;
-    st->decay = (float)(hp.lr * hp.weight_decay);
+    st->inv_scale = scale ? scale->inv_scale : hp.inv_loss_scale;
+    const double bc1 = 1.0 - pow(hp.beta1, (double)t);
+    const double bc2 = 1.0 - pow(hp.beta2, (double)t);
+    st->bc1 = bc1;
+    st->bc2 = bc2;
+    st->inv_bc1 = 1.0 / bc1;
+    st->inv_bc2 = 1.0 / bc2;
 }
 
 // Dynamic loss scaling (Micikevicius et al., "Mixed Precision Training"): one
@@ -616,11 +728,18 @@ __global__ void loss_scale_update(zero_loss_scaler c, const zero_grad_stats_t *s
     d->overflows = overflows;
 }
 
+// Hyper-parameters of the element update, fp64, from the host: beta1, beta2,
+// eps and lr as given, 1 - beta1, 1 - beta2 and lr * wd formed in fp64.
+struct AdamHyper {
+    double b1, omb1, b2, omb2, eps, lr, lrwd;
+};
+
 struct AdamArgs {
     const uint16_t *g;
     float *master, *m, *v;
     uint16_t *p;
     const zero_adam_state_t *st;
+    AdamHyper h;
     uint64_t n;
     uint64_t head;     // elements [0, head) go element by element
     uint64_t nchunks;  // then nchunks chunks of 8 elements
@@ -628,32 +747,67 @@ struct AdamArgs {
     uint32_t p_phase;  // same for p
 };
 
+// Everything one element's update needs: the host's hyper-parameters and the
+// step's device scalars (inverse loss scale, clip coefficient, bias
+// corrections and their correctly rounded reciprocals).
 struct Coeffs {
-    float grad_mult, step_size, inv_sqrt_bc2, b1, omb1, b2, omb2, eps, decay;
+    AdamHyper h;
+    double inv, coef, bc1, bc2, inv_bc1, inv_bc2;
 };
 
+// a / b rounded to nearest, given rb = RN(1 / b): the product a * rb is
+// within one ulp of the quotient, and one fused correction with the exact
+// residual a - b q0 rounds it correctly (Markstein's theorem: P. Markstein,
+// "Computation of elementary functions on the IBM RISC System/6000
+// processor", IBM J. Res. Dev. 34(1), 1990), for finite a and b without
+// underflow, which holds here (|a| is 0 or above 2^-160, b in (0, 1]).
+// SIGNED_ZERO: a may be -0, which is returned as it is (a / b keeps the sign
+// of a zero dividend; the correction would give +0).
+template <bool SIGNED_ZERO>
+__device__ __forceinline__ double div_by(double a, double b, double rb)
+{
+#pragma clang fp contract(off)
+    const double q0 = a * rb;
+    const double r = __builtin_fma(-b, q0, a);
+    const double q = __builtin_fma(r, rb, q0);
+    if constexpr (SIGNED_ZERO)
+        return a == 0.0 ? a : q;
+    else
+        return q;
+}
+
+// One element of AdamW in fp64, every operation correctly rounded and none
+// fused, in the order the update is written: the fp32 results are the
+// roundings of the exact fp64 sequence.
 __device__ __forceinline__ void adamw_elem(const Coeffs &k, float graw, float &th, float &m,
                                            float &v)
 {
-    const float g = graw * k.grad_mult;
-    const float m1 = fmaf(k.b1, m, k.omb1 * g);
-    const float v1 = fmaf(k.b2, v, (k.omb2 * g) * g);
-    const float den = fmaf(sqrtf(v1), k.inv_sqrt_bc2, k.eps);  // correctly rounded
-    const float ratio = m1 / den;                              // correctly rounded
-    const float th1 = fmaf(-k.decay, th, th);
-    th = fmaf(-k.step_size, ratio, th1);
-    m = m1;
-    v = v1;
+#pragma clang fp contract(off)
+    const double g = ((double)graw * k.inv) * k.coef;
+    const double m1 = k.h.b1 * (double)m + k.h.omb1 * g;
+    const double v1 = k.h.b2 * (double)v + (k.h.omb2 * g) * g;
+    const double m_hat = div_by<true>(m1, k.bc1, k.inv_bc1);
+    const double v_hat = div_by<false>(v1, k.bc2, k.inv_bc2);  // v1 is +0 or positive
+    const double p = (double)th;
+    const double p1 = (p - k.h.lrwd * p) - (k.h.lr * m_hat) / (__builtin_sqrt(v_hat) + k.h.eps);
+    th = (float)p1;
+    m = (float)m1;
+    v = (float)v1;
 }
 
 constexpr int kAdamUnroll = ZERO_ADAM_UNROLL;
 
 // Dynamic LDS reserved by every AdamW block, which uses none.  Of gfx950's
-// 160 KiB of LDS per CU it leaves room for two blocks (eight waves) per CU,
-// below the five that the registers allow.  With fewer streams in flight at
-// once HBM serves the kernel's five arrays faster: on the 1.5B shard 7.03 ms
-// per step against 7.13 ms at five blocks per CU, and 7.73 ms at one.
-constexpr size_t kAdamLdsReserve = 64 * 1024;
+// 160 KiB of LDS per CU it leaves room for three blocks (twelve waves) per
+// CU, below the four or five that the registers allow.  With fewer streams
+// in flight at once HBM serves the kernel's five arrays faster, and three
+// blocks hide the fp64 arithmetic: on the 1.5B shard 7.02 ms per step
+// against 7.40 ms at two blocks per CU and 7.17 ms at four; on the 13B
+// shard 57.9 ms against 61.0 and 59.2.
+#ifndef ZERO_ADAM_LDS
+#define ZERO_ADAM_LDS (48 * 1024)
+#endif
+constexpr size_t kAdamLdsReserve = ZERO_ADAM_LDS;
 
 // Whether chunk c's right neighbour c + 1 is not held by the next lane of the
 // same wave: c is on the last lane, or c + 1 is past the body.  Chunks of one
@@ -669,8 +823,7 @@ __global__ void __launch_bounds__(kBlock) adamw_stream(AdamArgs a)
     const zero_adam_state_t *st = a.st;
     if (st->skip)
         return;
-    const Coeffs k{st->grad_mult, st->step_size, st->inv_sqrt_bc2, st->beta1, st->one_minus_beta1,
-                   st->beta2, st->one_minus_beta2, st->eps, st->decay};
+    const Coeffs k{a.h, st->inv_scale, st->coef, st->bc1, st->bc2, st->inv_bc1, st->inv_bc2};
 
     // aligned views of the body [head, head + 8 nchunks)
     float4 *th4 = reinterpret_cast<float4 *>(a.master + a.head);
@@ -769,6 +922,126 @@ __global__ void __launch_bounds__(kBlock) adamw_stream(AdamArgs a)
     }
 }
 
+// ------------------------------------------------- AdamW from tensor lists
+// The same update over a range of the tensors' list-order flat stream, with
+// every gradient read in place from its per-tensor buffer ("ZeRO: Memory
+// Optimizations Toward Training Trillion Parameter Models", paper summary
+// page, section ZeRO-R > CB: the gradients need no gathered copy when the
+// per-tensor buffers already hold the rank's final gradients).  The segment
+// table is the gather's: tiles follow the 8-element chunks of the fp32
+// arrays (a notional 16-bit destination at phase (8 - head) % 8 has its lines
+// exactly there), each tile inside one tensor's segment; a segment's
+// elements outside whole chunks (at most 7 at each end) are updated one by
+// one by the threads of its first tile.
+struct AdamSegArgs {
+    FlatArgs t;            // segment table (t.dst is unused)
+    float *master, *m, *v; // element 0 of the range
+    uint16_t *p;
+    const zero_adam_state_t *st;
+    AdamHyper h;
+    uint64_t head;         // elements before the fp32 arrays' first 16-byte boundary
+    uint32_t p_phase;      // slot (0..7) of element `head` of p within its 16-byte line
+};
+static_assert(sizeof(AdamSegArgs) <= 4096, "kernel arguments are limited to 4 KiB");
+
+template <bool GBF16, bool PBF16, bool P_ALIGNED>
+__global__ void __launch_bounds__(kBlock) adamw_segments(AdamSegArgs a)
+{
+    const zero_adam_state_t *st = a.st;
+    if (st->skip)
+        return;
+    const Coeffs k{a.h, st->inv_scale, st->coef, st->bc1, st->bc2, st->inv_bc1, st->inv_bc2};
+    // tiles renumbered so that each XCD (block i runs on XCD i % 8) streams a
+    // contiguous eighth of the range; the grid is a multiple of 8
+    const uint32_t per_xcd = gridDim.x / 8;
+    const uint32_t tile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (tile >= a.t.n_tiles)
+        return;
+    const uint32_t s = find_segment(a.t, tile);
+    const uint64_t e_lo = a.t.seg_lo[s], e_hi = a.t.seg_lo[s + 1];
+    const uint64_t ph = a.t.dst_phase;
+    const uint64_t c0 = (e_lo + ph + 7) / 8, c1 = (e_hi + ph) / 8;  // whole chunks, line units
+    const bool has_full = c1 > c0;
+    const uint64_t kt = tile - a.t.tile_lo[s];  // tile within the segment
+    const uint16_t *src = reinterpret_cast<const uint16_t *>(a.t.src[s]);  // gradient of e_lo
+    if (kt == 0) {  // the segment's elements outside whole chunks, one per thread
+        const uint64_t head_end = has_full ? c0 * 8 - ph : e_hi;
+        const uint64_t tail_beg = has_full ? c1 * 8 - ph : e_hi;
+        const uint64_t n_head = head_end - e_lo, n_tail = e_hi - tail_beg;
+        if (threadIdx.x < n_head + n_tail) {
+            const uint64_t e =
+                threadIdx.x < n_head ? e_lo + threadIdx.x : tail_beg + (threadIdx.x - n_head);
+            float t = a.master[e], mv = a.m[e], vw = a.v[e];
+            adamw_elem(k, to_f32<GBF16>(ld_global(src + (e - e_lo))), t, mv, vw);
+            a.master[e] = t;
+            a.m[e] = mv;
+            a.v[e] = vw;
+            a.p[e] = (uint16_t)from_f32<PBF16>(t);
+        }
+    }
+    if (!has_full)
+        return;
+    const uint64_t t_beg = kt * kFlatTileChunks;
+    const uint64_t t_end = t_beg + kFlatTileChunks < c1 - c0 ? t_beg + kFlatTileChunks : c1 - c0;
+    const uint64_t j = t_beg + threadIdx.x;  // this lane's chunk within the segment
+    if (j >= t_end)
+        return;
+    // chunk of the segment's first whole line: line L holds elements
+    // [8L - ph, 8L - ph + 8) = chunk L - 1 when head > 0, chunk L otherwise
+    const uint64_t c = c0 - (a.head != 0) + j;
+    const bool last = threadIdx.x % 64 == 63 || j + 1 >= t_end;  // no right neighbour
+    // the gradients of chunk c: elements head + 8c .. + 7 of the range
+    const uintptr_t g0 = (uintptr_t)(src + (a.head + 8 * (c0 - (a.head != 0)) - e_lo));
+    const uint32_t gsb = (uint32_t)(g0 & 15u);  // uniform in the segment
+    const uint4 *gl = reinterpret_cast<const uint4 *>(g0 - gsb) + j;
+    float4 *th4 = reinterpret_cast<float4 *>(a.master + a.head);
+    float4 *m4 = reinterpret_cast<float4 *>(a.m + a.head);
+    float4 *v4 = reinterpret_cast<float4 *>(a.v + a.head);
+    uint16_t *pl = a.p + a.head - a.p_phase;  // aligned line holding element `head`
+    uint4 gw = ld_global(gl), ghi = make_uint4(0, 0, 0, 0);
+    if (gsb != 0 && last)  // the next line holds live gradients of this chunk
+        ghi = ld_global(gl + 1);
+    float4 th[2] = {ld_stream(th4 + 2 * c), ld_stream(th4 + 2 * c + 1)};
+    float4 mm[2] = {ld_stream(m4 + 2 * c), ld_stream(m4 + 2 * c + 1)};
+    float4 vv[2] = {ld_stream(v4 + 2 * c), ld_stream(v4 + 2 * c + 1)};
+    if (gsb != 0) {
+        const uint4 nxt = shfl_line_down(gw);
+        gw = shift_lines_rt(gw, last ? ghi : nxt, gsb);
+    }
+    const uint32_t gws[4] = {gw.x, gw.y, gw.z, gw.w};
+    float *t = reinterpret_cast<float *>(th);
+    float *mv = reinterpret_cast<float *>(mm);
+    float *vw = reinterpret_cast<float *>(vv);
+    uint32_t ph16[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t w = gws[e / 2];
+        const float graw = (e & 1) ? hi_to_f32<GBF16>(w) : to_f32<GBF16>(w & 0xffffu);
+        adamw_elem(k, graw, t[e], mv[e], vw[e]);
+        ph16[e] = from_f32<PBF16>(t[e]);
+    }
+    st_stream(th4 + 2 * c, th[0]); st_stream(th4 + 2 * c + 1, th[1]);
+    st_stream(m4 + 2 * c, mm[0]);  st_stream(m4 + 2 * c + 1, mm[1]);
+    st_stream(v4 + 2 * c, vv[0]);  st_stream(v4 + 2 * c + 1, vv[1]);
+    if constexpr (P_ALIGNED) {
+        store_run<0, 8>(pl + 8 * c, ph16);
+    } else {
+        // as in adamw_stream: a lane with a left neighbour writes the whole line
+        // it shares with it; the first lane of a wave writes its head, and a
+        // lane without a right neighbour also its tail
+        const uint4 own = make_uint4(ph16[0] | ph16[1] << 16, ph16[2] | ph16[3] << 16,
+                                     ph16[4] | ph16[5] << 16, ph16[6] | ph16[7] << 16);
+        const uint4 prev = shfl_line_up(own);
+        if (threadIdx.x % 64 != 0)
+            st_stream(reinterpret_cast<uint4 *>(pl + 8 * c),
+                      shift_lines_rt(prev, own, 16 - 2 * a.p_phase));
+        else
+            store_head_rt(pl + 8 * c, ph16, a.p_phase);
+        if (last)
+            store_tail_rt(pl + 8 * c + 8, ph16, a.p_phase);
+    }
+}
+
 // ------------------------------------------------------------ host helpers
 inline bool aligned(const void *p, uintptr_t k) { return ((uintptr_t)p & (k - 1)) == 0; }
 
@@ -815,7 +1088,15 @@ uint32_t resident_blocks(K kernel, size_t dyn_lds = 0)
 // Blocks of one launch.  A dispatch is kept below 2^31 work-items, inside
 // both the dispatch packet's 32-bit grid size and the runtime's int-typed grid
 // limits; a multiple of 8, so that a capped grid spans whole rounds of XCDs.
-constexpr uint64_t kMaxLaunchBlocks = 0x7fffffffu / kBlock / 8 * 8;
+// A smaller cap (a multiple of 8) can be set at build time to exercise the
+// multi-launch and multi-round paths on small inputs.
+#ifndef ZERO_MAX_LAUNCH_BLOCKS
+#define ZERO_MAX_LAUNCH_BLOCKS (0x7fffffffu / kBlock / 8 * 8)
+#endif
+constexpr uint64_t kMaxLaunchBlocks = ZERO_MAX_LAUNCH_BLOCKS;
+static_assert(kMaxLaunchBlocks >= 8 && kMaxLaunchBlocks % 8 == 0 &&
+                  kMaxLaunchBlocks <= 0x7fffffffu / kBlock,
+              "launch cap: a positive multiple of 8 below 2^31 work-items");
 
 inline uint32_t grid_for(uint64_t work_items, uint64_t per_block, uint32_t max_blocks)
 {
@@ -855,39 +1136,52 @@ uint64_t flatten_tiles_max(const uint64_t *numel, uint32_t n_tensors, uint64_t r
     return tiles ? tiles : 1;
 }
 
-// Shared body of the two gather entry points.  mode: kCopy or a stats mode;
-// part: per-tile partials (stats modes), part_bytes long, which the sources
-// must not overlap either.  *n_tiles: tiles used.
-zero_status flatten_impl(const char *what, const void *const *tensor_ptrs, const uint64_t *numel,
-                         uint32_t n_tensors, zero_dtype dt, uint64_t range_begin, uint64_t count,
-                         void *dst, int mode, double *part, size_t part_bytes, hipStream_t stream,
-                         uint64_t *n_tiles)
+// Checks the tensor table and the range [range_begin, range_begin + count)
+// of the flat stream; *range_end receives its end.
+zero_status check_range(const char *what, const void *const *tensor_ptrs, const uint64_t *numel,
+                        uint32_t n_tensors, uint64_t range_begin, uint64_t count,
+                        uint64_t *range_end)
 {
-    *n_tiles = 0;
     if (n_tensors > 0 && (!tensor_ptrs || !numel))
         return fail(ZERO_EINVAL, "%s: NULL tensor table", what);
-    const uint64_t es = dt == ZERO_F32 ? 4 : 2;
     uint64_t psi = 0;
     for (uint32_t i = 0; i < n_tensors; ++i)
         if (__builtin_add_overflow(psi, numel[i], &psi))
             return fail(ZERO_EINVAL, "%s: total size overflows", what);
-    uint64_t range_end;
-    if (__builtin_add_overflow(range_begin, count, &range_end) || range_end > psi)
+    if (__builtin_add_overflow(range_begin, count, range_end) || *range_end > psi)
         return fail(ZERO_EINVAL, "%s: range [%llu, +%llu) beyond %llu elements", what,
                     (unsigned long long)range_begin, (unsigned long long)count,
                     (unsigned long long)psi);
-    if (count == 0)
-        return ZERO_OK;
-    if (!dst)
-        return fail(ZERO_EINVAL, "%s: NULL dst", what);
-    if (!aligned(dst, es))
-        return fail(ZERO_EALIGN, "%s: dst not %llu-byte aligned", what, (unsigned long long)es);
-    if (count > UINT64_MAX / es)
+    if (count > UINT64_MAX / 4)
         return fail(ZERO_EINVAL, "%s: count too large", what);
+    return ZERO_OK;
+}
 
-    // tiles of the segment [d_lo, d_hi) of the destination: its full 16-byte
-    // lines in tiles, or one tile for a segment without a full line
-    const uint64_t V = 16 / es, ph = ((uintptr_t)dst & 15u) / es;
+// A device buffer that the tensors read by a segment launch must not overlap.
+struct Guard {
+    const void *p;
+    uint64_t bytes;
+    const char *name;
+};
+
+// Cuts the range [range_begin, range_end) of the tensors' flat stream into
+// segment tables and launches each one with launch(a): every intersecting
+// tensor is one segment, or several when a launch has room for fewer tiles.
+// Tiles follow the 16-byte lines of a notional destination whose element 0
+// sits at element phase ph (es-byte elements): a segment's full lines go in
+// tiles of kFlatTileChunks lines, and a segment without a full line takes one
+// tile.  a.tile_base counts the tiles of earlier launches.  Every
+// intersecting tensor must be non-NULL, aligned to es and overlap none of
+// the guards.  *n_tiles: tiles used in all.
+template <typename Launch>
+zero_status segment_launches(const char *what, const void *const *tensor_ptrs,
+                             const uint64_t *numel, uint32_t n_tensors, uint64_t es,
+                             uint64_t range_begin, uint64_t range_end, uint64_t ph,
+                             const Guard *guards, int n_guards, FlatArgs &a, Launch launch,
+                             uint64_t *n_tiles)
+{
+    *n_tiles = 0;
+    const uint64_t V = 16 / es;
     auto seg_tiles = [&](uint64_t d_lo, uint64_t d_hi) {
         const uint64_t c0 = (d_lo + ph + V - 1) / V, c1 = (d_hi + ph) / V;
         const uint64_t full = c1 > c0 ? c1 - c0 : 0;
@@ -909,34 +1203,24 @@ zero_status flatten_impl(const char *what, const void *const *tensor_ptrs, const
         if (!aligned(src, es))
             return fail(ZERO_EALIGN, "%s: tensor %u not %llu-byte aligned", what, i,
                         (unsigned long long)es);
-        if (overlap(src + (lo - t_lo) * es, (hi - lo) * es, dst, count * es))
-            return fail(ZERO_EINVAL, "%s: dst overlaps tensor %u", what, i);
-        if (overlap(src + (lo - t_lo) * es, (hi - lo) * es, part, part_bytes))
-            return fail(ZERO_EINVAL, "%s: workspace overlaps tensor %u", what, i);
+        for (int k = 0; k < n_guards; ++k)
+            if (overlap(src + (lo - t_lo) * es, (hi - lo) * es, guards[k].p, guards[k].bytes))
+                return fail(ZERO_EINVAL, "%s: %s overlaps tensor %u", what, guards[k].name, i);
     }
 
-    FlatArgs a{};
-    a.dst = (char *)dst;
-    a.part = part;
+    a.n_segs = 0;
+    a.tile_base = 0;
     a.dst_phase = (uint32_t)ph;
     uint64_t launch_tiles = 0;  // tiles of the segments in the table
     // launches the segments in the table, after completing the search tables
-    auto launch = [&]() -> zero_status {
+    auto flush = [&]() -> zero_status {
         a.n_tiles = (uint32_t)launch_tiles;
         a.tile_lo[a.n_segs] = a.n_tiles;
         for (uint32_t i = a.n_segs + 1; i < (uint32_t)(kMaxSegs + kSegFan); ++i)
             a.tile_lo[i] = kTilePad;
         for (int j = 0; j < kSegCoarse; ++j)
             a.coarse[j] = a.tile_lo[kSegFan * j];
-        zero_status st;
-        if (es == 4)
-            st = flatten_launch<4, kCopy>(a, stream);
-        else if (mode == kStatsF16)
-            st = flatten_launch<2, kStatsF16>(a, stream);
-        else if (mode == kStatsBF16)
-            st = flatten_launch<2, kStatsBF16>(a, stream);
-        else
-            st = flatten_launch<2, kCopy>(a, stream);
+        const zero_status st = launch(a);
         a.tile_base += launch_tiles;
         a.n_segs = 0;
         launch_tiles = 0;
@@ -974,12 +1258,51 @@ zero_status flatten_impl(const char *what, const void *const *tensor_ptrs, const
             d_lo = d_end;
             if (a.n_segs == kMaxSegs || launch_tiles == kMaxLaunchTiles ||
                 (d_lo == d_hi && hi == range_end))
-                if (zero_status st = launch(); st != ZERO_OK)
+                if (zero_status st = flush(); st != ZERO_OK)
                     return st;
         }
     }
     *n_tiles = a.tile_base;
     return ZERO_OK;
+}
+
+// Shared body of the gather entry points.  mode: kCopy or a stats mode; part:
+// per-tile partials (stats modes), part_bytes long, which the sources must
+// not overlap either.  *n_tiles: tiles used.
+zero_status flatten_impl(const char *what, const void *const *tensor_ptrs, const uint64_t *numel,
+                         uint32_t n_tensors, zero_dtype dt, uint64_t range_begin, uint64_t count,
+                         void *dst, int mode, double *part, size_t part_bytes, hipStream_t stream,
+                         uint64_t *n_tiles)
+{
+    *n_tiles = 0;
+    uint64_t range_end;
+    if (zero_status st = check_range(what, tensor_ptrs, numel, n_tensors, range_begin, count,
+                                     &range_end);
+        st != ZERO_OK)
+        return st;
+    if (count == 0)
+        return ZERO_OK;
+    const uint64_t es = dt == ZERO_F32 ? 4 : 2;
+    if (!dst)
+        return fail(ZERO_EINVAL, "%s: NULL dst", what);
+    if (!aligned(dst, es))
+        return fail(ZERO_EALIGN, "%s: dst not %llu-byte aligned", what, (unsigned long long)es);
+    const Guard guards[2] = {{dst, count * es, "dst"}, {part, part_bytes, "workspace"}};
+    FlatArgs a{};
+    a.dst = (char *)dst;
+    a.part = part;
+    auto launch = [&](FlatArgs &t) -> zero_status {
+        if (es == 4)
+            return flatten_launch<4, kCopy>(t, stream);
+        switch (mode) {
+        case kStatsF16: return flatten_launch<2, kStatsF16>(t, stream);
+        case kStatsBF16: return flatten_launch<2, kStatsBF16>(t, stream);
+        default: return flatten_launch<2, kCopy>(t, stream);
+        }
+    };
+    const uint64_t ph = ((uintptr_t)dst & 15u) / es;
+    return segment_launches(what, tensor_ptrs, numel, n_tensors, es, range_begin, range_end, ph,
+                            guards, 2, a, launch, n_tiles);
 }
 
 }  // namespace
@@ -1038,61 +1361,92 @@ extern "C" zero_status zero_grad_stats_workspace(uint64_t n, size_t *bytes)
     return ZERO_OK;
 }
 
+namespace {
+// Checks shared by the two statistics entry points (everything but the
+// workspace).  Returns the inverse loss scale to pass to the kernels.
+zero_status check_stats_args(const char *what, const void *grad, zero_dtype gdt, uint64_t n,
+                             double *inv_loss_scale, const zero_loss_scale_t *d_scale,
+                             const zero_grad_stats_t *d_stats)
+{
+    if (gdt != ZERO_F16 && gdt != ZERO_BF16)
+        return fail(ZERO_EINVAL, "%s: gradient dtype must be F16 or BF16", what);
+    if (!d_stats)
+        return fail(ZERO_EINVAL, "%s: NULL d_stats", what);
+    if (!d_scale && !(std::isfinite(*inv_loss_scale) && *inv_loss_scale > 0.0))
+        return fail(ZERO_EINVAL, "%s: inv_loss_scale must be finite and > 0", what);
+    if (d_scale)
+        *inv_loss_scale = 1.0;  // unused: the kernel reads the device state
+    if (n > 0 && !grad)
+        return fail(ZERO_EINVAL, "%s: NULL grad", what);
+    if (n > UINT64_MAX / 4)
+        return fail(ZERO_EINVAL, "%s: n too large", what);
+    if (!aligned(grad, 2) || !aligned(d_stats, 8) || !aligned(d_scale, 8))
+        return fail(ZERO_EALIGN, "%s: misaligned pointer", what);
+    if (overlap(d_stats, sizeof *d_stats, grad, 2 * n) ||
+        (d_scale && overlap(d_scale, sizeof *d_scale, d_stats, sizeof *d_stats)))
+        return fail(ZERO_EINVAL, "%s: overlapping buffers", what);
+    return ZERO_OK;
+}
+
+// The aligned body of n gradients at `grad`: elements [0, head) precede the
+// first 16-byte line, nchunks whole lines follow, then [tail_beg, n).
+struct StatsLayout {
+    uint64_t head, nchunks, tail_beg, tiles;
+};
+
+StatsLayout stats_layout(const void *grad, uint64_t n)
+{
+    StatsLayout l;
+    const uint64_t ph = ((uintptr_t)grad & 15u) / 2;
+    l.head = (8 - ph) % 8;
+    if (l.head > n) l.head = n;
+    l.nchunks = (n - l.head) / 8;
+    l.tail_beg = l.head + 8 * l.nchunks;
+    l.tiles = (l.nchunks + kStatsTileLines - 1) / kStatsTileLines;
+    if (l.tiles == 0) l.tiles = 1;  // tile 0 also takes the elements outside the lines
+    return l;
+}
+}  // namespace
+
 extern "C" zero_status zero_grad_stats(const void *grad, zero_dtype gdt, uint64_t n,
                                        double inv_loss_scale, const zero_loss_scale_t *d_scale,
                                        void *workspace, size_t ws_bytes,
                                        zero_grad_stats_t *d_stats, void *stream)
 {
-    if (gdt != ZERO_F16 && gdt != ZERO_BF16)
-        return fail(ZERO_EINVAL, "zero_grad_stats: gradient dtype must be F16 or BF16");
-    if (!d_stats)
-        return fail(ZERO_EINVAL, "zero_grad_stats: NULL d_stats");
-    if (!d_scale && !(std::isfinite(inv_loss_scale) && inv_loss_scale > 0.0))
-        return fail(ZERO_EINVAL, "zero_grad_stats: inv_loss_scale must be finite and > 0");
-    if (d_scale)
-        inv_loss_scale = 1.0;  // unused: the kernel reads the device state
-    if (n > 0 && !grad)
-        return fail(ZERO_EINVAL, "zero_grad_stats: NULL grad");
-    if (n > UINT64_MAX / 4)
-        return fail(ZERO_EINVAL, "zero_grad_stats: n too large");
+    const char *what = "zero_grad_stats";
+    if (zero_status st = check_stats_args(what, grad, gdt, n, &inv_loss_scale, d_scale, d_stats);
+        st != ZERO_OK)
+        return st;
     if (!workspace)
-        return fail(ZERO_EINVAL, "zero_grad_stats: NULL workspace");
+        return fail(ZERO_EINVAL, "%s: NULL workspace", what);
     const size_t need = stats_workspace_bytes(n);
     if (ws_bytes < need)
-        return fail(ZERO_ENOSPC, "zero_grad_stats: workspace %zu bytes < %zu", ws_bytes, need);
-    if (!aligned(grad, 2) || !aligned(workspace, 16) || !aligned(d_stats, 8) ||
-        !aligned(d_scale, 8))
-        return fail(ZERO_EALIGN, "zero_grad_stats: misaligned pointer");
+        return fail(ZERO_ENOSPC, "%s: workspace %zu bytes < %zu", what, ws_bytes, need);
+    if (!aligned(workspace, 16))
+        return fail(ZERO_EALIGN, "%s: misaligned workspace", what);
     if (overlap(workspace, ws_bytes, d_stats, sizeof *d_stats) ||
-        overlap(workspace, ws_bytes, grad, 2 * n) || overlap(d_stats, sizeof *d_stats, grad, 2 * n) ||
-        (d_scale && (overlap(d_scale, sizeof *d_scale, workspace, ws_bytes) ||
-                     overlap(d_scale, sizeof *d_scale, d_stats, sizeof *d_stats))))
-        return fail(ZERO_EINVAL, "zero_grad_stats: overlapping buffers");
+        overlap(workspace, ws_bytes, grad, 2 * n) ||
+        (d_scale && overlap(d_scale, sizeof *d_scale, workspace, ws_bytes)))
+        return fail(ZERO_EINVAL, "%s: overlapping buffers", what);
     hipStream_t s = (hipStream_t)stream;
-    const uint64_t ph = ((uintptr_t)grad & 15u) / 2;
-    uint64_t head = (8 - ph) % 8;
-    if (head > n) head = n;
-    const uint64_t nchunks = (n - head) / 8;
-    const uint64_t tail_beg = head + 8 * nchunks;
-    uint64_t tiles = (nchunks + kStatsTileLines - 1) / kStatsTileLines;
-    if (tiles == 0) tiles = 1;  // tile 0 also takes the elements outside the lines
+    const StatsLayout l = stats_layout(grad, n);
     double *part = (double *)workspace;
     const uint16_t *g = (const uint16_t *)grad;
     // one tile per block, in launches of at most kMaxLaunchBlocks blocks
-    for (uint64_t t0 = 0; t0 < tiles; t0 += kMaxLaunchBlocks) {
-        const uint32_t grid = (uint32_t)(tiles - t0 < kMaxLaunchBlocks ? tiles - t0
-                                                                       : kMaxLaunchBlocks);
+    for (uint64_t t0 = 0; t0 < l.tiles; t0 += kMaxLaunchBlocks) {
+        const uint32_t grid = (uint32_t)(l.tiles - t0 < kMaxLaunchBlocks ? l.tiles - t0
+                                                                         : kMaxLaunchBlocks);
         if (gdt == ZERO_BF16)
-            hipLaunchKernelGGL(stats_pass1<true>, dim3(grid), dim3(kBlock), 0, s, g, head,
-                               nchunks, tail_beg, n, t0, part);
+            hipLaunchKernelGGL(stats_pass1<true>, dim3(grid), dim3(kBlock), 0, s, g, l.head,
+                               l.nchunks, l.tail_beg, n, t0, part);
         else
-            hipLaunchKernelGGL(stats_pass1<false>, dim3(grid), dim3(kBlock), 0, s, g, head,
-                               nchunks, tail_beg, n, t0, part);
+            hipLaunchKernelGGL(stats_pass1<false>, dim3(grid), dim3(kBlock), 0, s, g, l.head,
+                               l.nchunks, l.tail_beg, n, t0, part);
         const zero_status st = launch_status("zero_grad_stats pass 1");
         if (st != ZERO_OK)
             return st;
     }
-    return reduce_partials(part, tiles, inv_loss_scale, d_scale, d_stats, s);
+    return reduce_partials(part, l.tiles, inv_loss_scale, d_scale, d_stats, s);
 }
 
 extern "C" zero_status zero_bucket_flatten_stats_workspace(const uint64_t *numel, uint32_t n_tensors,
@@ -1229,6 +1583,8 @@ extern "C" zero_status zero_adam_step(const zero_adamw *hp, const void *grad, ze
     a.v = exp_avg_sq;
     a.p = (uint16_t *)param_out;
     a.st = d_state;
+    a.h = AdamHyper{hp->beta1, 1.0 - hp->beta1, hp->beta2, 1.0 - hp->beta2, hp->eps, hp->lr,
+                    hp->lr * hp->weight_decay};
     a.n = n;
     const uintptr_t fph = ((uintptr_t)master & 15u) / 4;
     const bool same = fph == ((uintptr_t)exp_avg & 15u) / 4 && fph == ((uintptr_t)exp_avg_sq & 15u) / 4;
@@ -1253,6 +1609,166 @@ extern "C" zero_status zero_adam_step(const zero_adamw *hp, const void *grad, ze
     else if (pb) launch_adam<false, true>(a, work, s);
     else launch_adam<false, false>(a, work, s);
     return launch_status("zero_adam_step");
+}
+
+// ------------------------------------------------ steps from tensor lists
+extern "C" zero_status zero_grad_stats_tensors(const void *const *tensor_ptrs,
+                                               const uint64_t *numel, uint32_t n_tensors,
+                                               zero_dtype gdt, uint64_t range_begin,
+                                               uint64_t count, double inv_loss_scale,
+                                               const zero_loss_scale_t *d_scale,
+                                               void *workspace, size_t ws_bytes,
+                                               zero_grad_stats_t *d_stats, void *stream)
+{
+    const char *what = "zero_grad_stats_tensors";
+    if (gdt != ZERO_F16 && gdt != ZERO_BF16)
+        return fail(ZERO_EINVAL, "%s: gradient dtype must be F16 or BF16", what);
+    if (!d_stats)
+        return fail(ZERO_EINVAL, "%s: NULL d_stats", what);
+    if (!d_scale && !(std::isfinite(inv_loss_scale) && inv_loss_scale > 0.0))
+        return fail(ZERO_EINVAL, "%s: inv_loss_scale must be finite and > 0", what);
+    if (d_scale)
+        inv_loss_scale = 1.0;  // unused: the kernel reads the device state
+    if (!workspace)
+        return fail(ZERO_EINVAL, "%s: NULL workspace", what);
+    uint64_t range_end;
+    if (zero_status st = check_range(what, tensor_ptrs, numel, n_tensors, range_begin, count,
+                                     &range_end);
+        st != ZERO_OK)
+        return st;
+    const size_t need = partials_bytes(flatten_tiles_max(numel, n_tensors, range_begin, range_end));
+    if (ws_bytes < need)
+        return fail(ZERO_ENOSPC, "%s: workspace %zu bytes < %zu", what, ws_bytes, need);
+    if (!aligned(workspace, 16) || !aligned(d_stats, 8) || !aligned(d_scale, 8))
+        return fail(ZERO_EALIGN, "%s: misaligned workspace, d_stats or d_scale", what);
+    if (overlap(workspace, ws_bytes, d_stats, sizeof *d_stats) ||
+        (d_scale && (overlap(d_scale, sizeof *d_scale, workspace, ws_bytes) ||
+                     overlap(d_scale, sizeof *d_scale, d_stats, sizeof *d_stats))))
+        return fail(ZERO_EINVAL, "%s: overlapping buffers", what);
+    hipStream_t s = (hipStream_t)stream;
+    const Guard guards[3] = {{workspace, ws_bytes, "workspace"},
+                             {d_stats, sizeof *d_stats, "d_stats"},
+                             {d_scale, d_scale ? sizeof *d_scale : 0, "d_scale"}};
+    FlatArgs a{};
+    a.part = (double *)workspace;
+    auto launch = [&](FlatArgs &t) -> zero_status {
+        const uint32_t grid = (t.n_tiles + kStatsTilesPerBlock - 1) / kStatsTilesPerBlock;
+        if (gdt == ZERO_BF16)
+            hipLaunchKernelGGL(stats_segments<true>, dim3(grid), dim3(kBlock), 0, s, t);
+        else
+            hipLaunchKernelGGL(stats_segments<false>, dim3(grid), dim3(kBlock), 0, s, t);
+        return launch_status(what);
+    };
+    uint64_t tiles = 0;
+    if (count > 0)
+        if (zero_status st = segment_launches(what, tensor_ptrs, numel, n_tensors, 2, range_begin,
+                                              range_end, 0, guards, 3, a, launch, &tiles);
+            st != ZERO_OK)
+            return st;
+    return reduce_partials((double *)workspace, tiles, inv_loss_scale, d_scale, d_stats, s);
+}
+
+namespace {
+template <bool GB, bool PB, bool PA>
+zero_status launch_adam_segments(const AdamSegArgs &a, hipStream_t s)
+{
+    const uint32_t grid = (a.t.n_tiles + 7) / 8 * 8;  // whole rounds of the 8 XCDs
+    hipLaunchKernelGGL((adamw_segments<GB, PB, PA>), dim3(grid), dim3(kBlock), kAdamLdsReserve,
+                       s, a);
+    return launch_status("zero_adam_step_tensors");
+}
+}  // namespace
+
+extern "C" zero_status zero_adam_step_tensors(const zero_adamw *hp,
+                                              const void *const *tensor_ptrs,
+                                              const uint64_t *numel, uint32_t n_tensors,
+                                              zero_dtype gdt, uint64_t range_begin,
+                                              uint64_t count, float *master, float *exp_avg,
+                                              float *exp_avg_sq, void *param_out, zero_dtype pdt,
+                                              const zero_grad_stats_t *d_stats,
+                                              const zero_loss_scale_t *d_scale,
+                                              zero_adam_state_t *d_state, void *stream)
+{
+    const char *what = "zero_adam_step_tensors";
+    if (!hp)
+        return fail(ZERO_EINVAL, "%s: NULL hyper-parameters", what);
+    if (!d_state)
+        return fail(ZERO_EINVAL, "%s: NULL d_state", what);
+    if ((gdt != ZERO_F16 && gdt != ZERO_BF16) || (pdt != ZERO_F16 && pdt != ZERO_BF16))
+        return fail(ZERO_EINVAL, "%s: grad and param dtypes must be F16 or BF16", what);
+    if (zero_status hs = zero::check_adamw(*hp, d_scale == nullptr, what); hs != ZERO_OK)
+        return hs;
+    uint64_t range_end;
+    if (zero_status st = check_range(what, tensor_ptrs, numel, n_tensors, range_begin, count,
+                                     &range_end);
+        st != ZERO_OK)
+        return st;
+    if (count > 0 && (!master || !exp_avg || !exp_avg_sq || !param_out))
+        return fail(ZERO_EINVAL, "%s: NULL array with count > 0", what);
+    if (!aligned(param_out, 2) || !aligned(master, 4) || !aligned(exp_avg, 4) ||
+        !aligned(exp_avg_sq, 4) || !aligned(d_state, 8) || !aligned(d_stats, 8) ||
+        !aligned(d_scale, 8))
+        return fail(ZERO_EALIGN, "%s: misaligned pointer", what);
+    const uintptr_t fph = ((uintptr_t)master & 15u) / 4;
+    if (count > 0 && (fph != ((uintptr_t)exp_avg & 15u) / 4 ||
+                      fph != ((uintptr_t)exp_avg_sq & 15u) / 4))
+        return fail(ZERO_EALIGN, "%s: master, exp_avg and exp_avg_sq must share their position "
+                    "within 16 bytes", what);
+    const void *buf[7] = {master, exp_avg, exp_avg_sq, param_out, d_state, d_stats, d_scale};
+    static const char *const names[7] = {"master", "exp_avg", "exp_avg_sq", "param_out",
+                                         "d_state", "d_stats", "d_scale"};
+    const uint64_t len[7] = {4 * count, 4 * count, 4 * count, 2 * count,
+                             sizeof(zero_adam_state_t), d_stats ? sizeof(zero_grad_stats_t) : 0,
+                             d_scale ? sizeof(zero_loss_scale_t) : 0};
+    for (int i = 0; i < 7; ++i)
+        for (int j = i + 1; j < 7; ++j)
+            if (overlap(buf[i], len[i], buf[j], len[j]))
+                return fail(ZERO_EINVAL, "%s: buffers %d and %d overlap", what, i, j);
+    // the tensors are checked against the outputs in segment_launches, before
+    // any element kernel runs; the scalar kernel only touches d_state
+    Guard guards[7];
+    for (int i = 0; i < 7; ++i)
+        guards[i] = Guard{buf[i], len[i], names[i]};
+    hipStream_t s = (hipStream_t)stream;
+    if (count == 0)
+        return zero::launch_adam_scalars(*hp, d_stats, d_scale, d_state, stream);
+
+    AdamSegArgs a{};
+    a.master = master;
+    a.m = exp_avg;
+    a.v = exp_avg_sq;
+    a.p = (uint16_t *)param_out;
+    a.st = d_state;
+    a.h = AdamHyper{hp->beta1, 1.0 - hp->beta1, hp->beta2, 1.0 - hp->beta2, hp->eps, hp->lr,
+                    hp->lr * hp->weight_decay};
+    a.head = (4 - fph) % 4;
+    if (a.head > count)
+        a.head = count;
+    a.p_phase = (uint32_t)((((uintptr_t)param_out & 15u) / 2 + a.head) % 8);
+    const bool gb = gdt == ZERO_BF16, pb = pdt == ZERO_BF16, pa = a.p_phase == 0;
+    bool scalars_done = false;
+    auto launch = [&](FlatArgs &t) -> zero_status {
+        if (!scalars_done) {  // after every tensor has been checked
+            if (zero_status st = zero::launch_adam_scalars(*hp, d_stats, d_scale, d_state, s);
+                st != ZERO_OK)
+                return st;
+            scalars_done = true;
+        }
+        a.t = t;
+        if (gb)
+            return pb ? (pa ? launch_adam_segments<true, true, true>(a, s)
+                            : launch_adam_segments<true, true, false>(a, s))
+                      : (pa ? launch_adam_segments<true, false, true>(a, s)
+                            : launch_adam_segments<true, false, false>(a, s));
+        return pb ? (pa ? launch_adam_segments<false, true, true>(a, s)
+                        : launch_adam_segments<false, true, false>(a, s))
+                  : (pa ? launch_adam_segments<false, false, true>(a, s)
+                        : launch_adam_segments<false, false, false>(a, s));
+    };
+    FlatArgs t{};
+    uint64_t tiles = 0;
+    return segment_launches(what, tensor_ptrs, numel, n_tensors, 2, range_begin, range_end,
+                            (8 - a.head) % 8, guards, 7, t, launch, &tiles);
 }
 
 extern "C" zero_status zero_loss_scale_init(const zero_loss_scaler *cfg, zero_loss_scale_t *d_scale,

@@ -13,9 +13,9 @@
 //      the gradients of chunk k+1 are copied device -> host while the host
 //      cores update chunk k, whose 16-bit parameters are then copied
 //      host -> device.
-// The host loop performs the same correctly rounded fp32 operations in the
-// same order as the device kernel (fma, sqrt, divide, round-to-nearest-even
-// to 16 bits), with the same fp32 scalars.
+// The host loop performs the same correctly rounded fp64 operations in the
+// same order as the device kernel (multiply, add, divide, sqrt, none fused),
+// with the same fp64 scalars, and the same roundings to fp32 and to 16 bits.
 #include <hip/hip_runtime_api.h>
 #include <omp.h>
 
@@ -31,9 +31,22 @@ namespace {
 
 constexpr uint64_t kMinChunk = 4096;  // elements per staging slot, at least
 
+// Hyper-parameters (beta1, beta2, eps, lr as given; 1 - beta1, 1 - beta2 and
+// lr * wd formed in fp64) and the step's scalars from the device state.
 struct Coeffs {
-    float grad_mult, step_size, inv_sqrt_bc2, b1, omb1, b2, omb2, eps, decay;
+    double b1, omb1, b2, omb2, eps, lr, lrwd, inv, coef, bc1, bc2, inv_bc1, inv_bc2;
 };
+
+// a / b from rb = RN(1 / b) and one fused correction, as the device does it
+// (the correctly rounded quotient, by Markstein's theorem); a zero dividend
+// as is where it may be -0.
+template <bool SIGNED_ZERO>
+inline double div_by(double a, double b, double rb)
+{
+    const double q0 = a * rb;
+    const double q = std::fma(std::fma(-b, q0, a), rb, q0);
+    return SIGNED_ZERO && a == 0.0 ? a : q;
+}
 
 inline float f16_to_f32(uint16_t h)
 {
@@ -71,19 +84,22 @@ inline uint16_t f32_to_bf16(float f)
 // One thread's contiguous part of a chunk.
 template <bool GBF16, bool PBF16>
 __attribute__((always_inline)) inline void
-adamw_body(const Coeffs k, const uint16_t *__restrict g, float *__restrict th,
+adamw_body(const Coeffs k, const uint16_t *__restrict g16, float *__restrict th,
            float *__restrict m, float *__restrict v, uint16_t *__restrict p, uint64_t cnt)
 {
     for (uint64_t i = 0; i < cnt; ++i) {
-        const float gr = (GBF16 ? bf16_to_f32(g[i]) : f16_to_f32(g[i])) * k.grad_mult;
-        const float m1 = std::fma(k.b1, m[i], k.omb1 * gr);
-        const float v1 = std::fma(k.b2, v[i], (k.omb2 * gr) * gr);
-        const float den = std::fma(std::sqrt(v1), k.inv_sqrt_bc2, k.eps);
-        const float th1 = std::fma(-k.decay, th[i], th[i]);
-        const float t = std::fma(-k.step_size, m1 / den, th1);
+        const double g = ((double)(GBF16 ? bf16_to_f32(g16[i]) : f16_to_f32(g16[i])) * k.inv) *
+                         k.coef;
+        const double m1 = k.b1 * (double)m[i] + k.omb1 * g;
+        const double v1 = k.b2 * (double)v[i] + (k.omb2 * g) * g;
+        const double m_hat = div_by<true>(m1, k.bc1, k.inv_bc1);
+        const double v_hat = div_by<false>(v1, k.bc2, k.inv_bc2);
+        const double p0 = (double)th[i];
+        const double p1 = (p0 - k.lrwd * p0) - (k.lr * m_hat) / (std::sqrt(v_hat) + k.eps);
+        const float t = (float)p1;
         th[i] = t;
-        m[i] = m1;
-        v[i] = v1;
+        m[i] = (float)m1;
+        v[i] = (float)v1;
         p[i] = PBF16 ? f32_to_bf16(t) : f32_to_f16(t);
     }
 }
@@ -208,8 +224,9 @@ extern "C" zero_status zero_offload_adam_step(const zero_adamw *hp, const void *
         return st;
     if (hs.skip || n == 0)
         return ZERO_OK;
-    const Coeffs k{hs.grad_mult, hs.step_size, hs.inv_sqrt_bc2, hs.beta1, hs.one_minus_beta1,
-                   hs.beta2, hs.one_minus_beta2, hs.eps, hs.decay};
+    const Coeffs k{hp->beta1, 1.0 - hp->beta1, hp->beta2, 1.0 - hp->beta2, hp->eps, hp->lr,
+                   hp->lr * hp->weight_decay, hs.inv_scale, hs.coef, hs.bc1, hs.bc2,
+                   hs.inv_bc1, hs.inv_bc2};
     const bool gb = gdt == ZERO_BF16, pb = pdt == ZERO_BF16;
     const RangeFn fn = gb ? (pb ? adamw_range_bb : adamw_range_bh)
                           : (pb ? adamw_range_hb : adamw_range_hh);
