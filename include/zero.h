@@ -210,6 +210,28 @@ zero_status zero_grad_stats(const void *grad, zero_dtype gdt, uint64_t n, double
                             const zero_loss_scale_t *d_scale, void *workspace, size_t ws_bytes,
                             zero_grad_stats_t *d_stats, void *stream);
 
+/* zero_grad_stats without a caller workspace and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * checks, errors and results as zero_grad_stats (overflow bit-exact; sq_norm
+ * in fp64, summed in a fixed order that depends only on n and grad's 16-byte
+ * phase, equal to zero_grad_stats's up to that order), except that the
+ * per-block partial sums live in the library's own device scratch: a static
+ * 64 KiB array (8192 fp64 partials) that every GPU the library runs on holds
+ * until the process ends.  The first pass folds the tiles of any n into at
+ * most 8192 partials, so no n is too large for the scratch (n is limited as
+ * for zero_grad_stats).  Each partial is written before it is read, so the
+ * scratch needs no clearing; but every call on one GPU shares that GPU's
+ * scratch, so calls that overlap in time on one GPU (on different streams,
+ * or from different threads without ordering) race and may return wrong
+ * statistics.  The first call on a device looks the scratch up with
+ * hipGetSymbolAddress (no allocation).  Errors: as zero_grad_stats
+ * (ZERO_EINVAL, ZERO_EALIGN), and ZERO_EDEVICE when there is no current
+ * device or the lookup fails. */
+zero_status zero_grad_stats_noalloc(const void *grad, zero_dtype gdt, uint64_t n,
+                                    double inv_loss_scale, const zero_loss_scale_t *d_scale,
+                                    zero_grad_stats_t *d_stats, void *stream);
+
 /* Bytes of device workspace that zero_bucket_flatten_stats needs for the
  * elements [range_begin, range_begin + count) of the tensors numel[]. */
 zero_status zero_bucket_flatten_stats_workspace(const uint64_t *numel, uint32_t n_tensors,

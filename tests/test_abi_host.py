@@ -194,6 +194,23 @@ def test_grad_stats_validation():
     assert _status(z.zero_grad_stats, g, "f16", n, 1.0, g + 64, need, st_, 0) == z.ZERO_EINVAL
 
 
+def test_grad_stats_noalloc_validation():
+    """The allocation-free variant checks its arguments like zero_grad_stats,
+    on the host, before it looks up its scratch or launches anything."""
+    n = 1 << 20
+    g, st_ = FAKE, FAKE + (8 << 20)
+    call = z.zero_grad_stats_noalloc
+    assert _status(call, g, "f32", n, 1.0, st_, 0) == z.ZERO_EINVAL
+    assert _status(call, g, "f16", n, 0.0, st_, 0) == z.ZERO_EINVAL
+    assert _status(call, g, "f16", n, float("nan"), st_, 0) == z.ZERO_EINVAL
+    assert _status(call, None, "f16", n, 1.0, st_, 0) == z.ZERO_EINVAL
+    assert _status(call, g, "f16", n, 1.0, None, 0) == z.ZERO_EINVAL
+    assert _status(call, g + 1, "f16", n, 1.0, st_, 0) == z.ZERO_EALIGN
+    assert _status(call, g, "f16", n, 1.0, st_ + 4, 0) == z.ZERO_EALIGN
+    assert _status(call, g, "f16", n, 1.0, g + 64, 0) == z.ZERO_EINVAL      # d_stats in grad
+    assert _status(call, g, "bf16", n, 1.0, st_, 0, st_ + 8) == z.ZERO_EINVAL  # d_scale on d_stats
+
+
 def test_flatten_validation():
     ts = [FAKE, FAKE + (1 << 20), None]
     numel = [100, 200, 50]

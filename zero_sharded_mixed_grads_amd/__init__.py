@@ -74,7 +74,7 @@ assert ctypes.sizeof(LossScaler) == 48 and ctypes.sizeof(LossScale) == 32
 EXPORTS = ("zero_status_str", "zero_last_error", "zero_partition", "zero_mem_bytes",
            "zero_bucket_plan", "zero_bucket_flatten", "zero_grad_stats_workspace",
            "zero_grad_stats", "zero_bucket_flatten_stats_workspace", "zero_bucket_flatten_stats",
-           "zero_grad_stats_tensors", "zero_adam_step_tensors",
+           "zero_grad_stats_noalloc", "zero_grad_stats_tensors", "zero_adam_step_tensors",
            "zero_adam_step", "zero_offload_staging_bytes", "zero_offload_adam_step",
            "zero_ckpt_save", "zero_ckpt_read_header", "zero_ckpt_load",
            "zero_loss_scale_init", "zero_loss_scale_update", "zero_state_layout")
@@ -109,6 +109,7 @@ def load(path: str):
     L.zero_grad_stats_workspace.argtypes = [U64, ctypes.POINTER(ctypes.c_size_t)]
     L.zero_grad_stats.argtypes = [VP, ctypes.c_int, U64, DBL, VP, VP, ctypes.c_size_t, VP,
                                   VP]
+    L.zero_grad_stats_noalloc.argtypes = [VP, ctypes.c_int, U64, DBL, VP, VP, VP]
     L.zero_grad_stats_tensors.argtypes = [ctypes.POINTER(VP), ctypes.POINTER(U64), U32,
                                           ctypes.c_int, U64, U64, DBL, VP, VP, ctypes.c_size_t,
                                           VP, VP]
@@ -246,6 +247,14 @@ def zero_grad_stats(grad, gdtype, n: int, inv_loss_scale: float, workspace, ws_b
     inv_loss_scale (read on the device)."""
     _check(lib().zero_grad_stats(_ptr(grad), _dtype(gdtype), n, inv_loss_scale, _ptr(d_scale),
                                  _ptr(workspace), ws_bytes, _ptr(d_stats), _stream(stream)))
+
+
+def zero_grad_stats_noalloc(grad, gdtype, n: int, inv_loss_scale: float, d_stats, stream=None,
+                            d_scale=None) -> None:
+    """zero_grad_stats with the library's own per-device scratch instead of a
+    caller workspace (calls on one device must not overlap)."""
+    _check(lib().zero_grad_stats_noalloc(_ptr(grad), _dtype(gdtype), n, inv_loss_scale,
+                                         _ptr(d_scale), _ptr(d_stats), _stream(stream)))
 
 
 def zero_bucket_flatten_stats_workspace(numel: Sequence[int], range_begin: int,

@@ -34,6 +34,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "zero_internal.h"
 
@@ -622,6 +623,21 @@ __global__ void __launch_bounds__(kBlock)
     const double t = block_sum(acc);
     if (threadIdx.x == 0)
         part[tile] = t;
+}
+
+// A fixed number of partials for any n: block b sums tiles b, b + gridDim.x,
+// b + 2 gridDim.x, ... and leaves one partial, part[b].
+template <bool BF16>
+__global__ void __launch_bounds__(kBlock)
+    stats_pass1_strided(const uint16_t *g, uint64_t head, uint64_t nchunks, uint64_t tail_beg,
+                        uint64_t n, uint64_t tiles, double *part)
+{
+    double acc = 0.0;
+    for (uint64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x)
+        stats_tile<BF16>(g, head, nchunks, tail_beg, n, tile, acc);
+    const double t = block_sum(acc);
+    if (threadIdx.x == 0)
+        part[blockIdx.x] = t;
 }
 
 // Block b sums partials [b*kReduceGroup, (b+1)*kReduceGroup) in a fixed order.
@@ -1447,6 +1463,74 @@ extern "C" zero_status zero_grad_stats(const void *grad, zero_dtype gdt, uint64_
             return st;
     }
     return reduce_partials(part, l.tiles, inv_loss_scale, d_scale, d_stats, s);
+}
+
+// ------------------------------------------- statistics without allocation
+// Device memory of zero_grad_stats_noalloc: the fp64 partials of its first
+// pass, one per block of a grid of at most kScratchPartials blocks (64 KiB).
+// Every GPU the library runs on holds its own copy until the process ends.
+// Host code reaches it only through the address that hipGetSymbolAddress
+// returns for the current device (the array's name is a host-side stand-in).
+constexpr uint64_t kScratchPartials = 8192;
+static_assert(kScratchPartials <= kFinalMax, "one block must finish the scratch partials");
+static __device__ __align__(256) double scratch[kScratchPartials];
+
+namespace {
+// Device address of `scratch` on the current device, looked up once per device.
+zero_status scratch_address(const char *what, double **out)
+{
+    constexpr int kMaxDev = 64;
+    static std::mutex mu;
+    static double *addr[kMaxDev];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev)
+        return fail(ZERO_EDEVICE, "%s: no current HIP device (or device index %d >= %d)", what,
+                    dev, kMaxDev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(ZERO_EDEVICE, "%s: hipGetSymbolAddress(scratch) on device %d: %s", what,
+                        dev, hipGetErrorString(e));
+        addr[dev] = (double *)p;
+    }
+    *out = addr[dev];
+    return ZERO_OK;
+}
+}  // namespace
+
+extern "C" zero_status zero_grad_stats_noalloc(const void *grad, zero_dtype gdt, uint64_t n,
+                                               double inv_loss_scale,
+                                               const zero_loss_scale_t *d_scale,
+                                               zero_grad_stats_t *d_stats, void *stream)
+{
+    const char *what = "zero_grad_stats_noalloc";
+    if (zero_status st = check_stats_args(what, grad, gdt, n, &inv_loss_scale, d_scale, d_stats);
+        st != ZERO_OK)
+        return st;
+    double *part = nullptr;
+    if (zero_status st = scratch_address(what, &part); st != ZERO_OK)
+        return st;
+    const StatsLayout l = stats_layout(grad, n);
+    // every tile is folded into one of at most kScratchPartials block partials,
+    // so the scratch holds the partials of any n
+    const uint64_t blocks = l.tiles < kScratchPartials ? l.tiles : kScratchPartials;
+    if (overlap(part, kScratchPartials * sizeof(double), grad, 2 * n) ||
+        overlap(part, kScratchPartials * sizeof(double), d_stats, sizeof *d_stats) ||
+        (d_scale && overlap(part, kScratchPartials * sizeof(double), d_scale, sizeof *d_scale)))
+        return fail(ZERO_EINVAL, "%s: a buffer overlaps the library's scratch", what);
+    hipStream_t s = (hipStream_t)stream;
+    const uint16_t *g = (const uint16_t *)grad;
+    if (gdt == ZERO_BF16)
+        hipLaunchKernelGGL(stats_pass1_strided<true>, dim3((uint32_t)blocks), dim3(kBlock), 0, s,
+                           g, l.head, l.nchunks, l.tail_beg, n, l.tiles, part);
+    else
+        hipLaunchKernelGGL(stats_pass1_strided<false>, dim3((uint32_t)blocks), dim3(kBlock), 0, s,
+                           g, l.head, l.nchunks, l.tail_beg, n, l.tiles, part);
+    if (zero_status st = launch_status("zero_grad_stats_noalloc pass 1"); st != ZERO_OK)
+        return st;
+    return reduce_partials(part, blocks, inv_loss_scale, d_scale, d_stats, s);
 }
 
 extern "C" zero_status zero_bucket_flatten_stats_workspace(const uint64_t *numel, uint32_t n_tensors,
