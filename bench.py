@@ -45,18 +45,21 @@ FLATTEN_BYTES_PER_PARAM = 4  # 16-bit read + write
 METRIC = "Adam-shard params/sec + achieved HBM GB/s vs peak (28 B/param)"
 PROFILES = os.path.join(ROOT, "profiles")
 CPU_SAMPLE_CAP = 1_000_000_000  # elements: the largest oracle sample (16 GB of host arrays)
-KERNEL_SRC = os.path.join(ROOT, "zero_sharded_mixed_grads_amd", "csrc", "zero_kernels.hip")
+# the AdamW kernel's sources: its own file and the device helpers it includes
+KERNEL_SRCS = [os.path.join(ROOT, "zero_sharded_mixed_grads_amd", "csrc", f)
+               for f in ("zero_adam.hip", "zero_device.h")]
 
 
 def kernel_source_hash() -> str:
-    """Hash of the kernel source's code: line comments, trailing blanks and
-    empty lines are dropped, so that editing comments keeps the stored
+    """Hash of the AdamW kernel sources' code: line comments, trailing blanks
+    and empty lines are dropped, so that editing comments keeps the stored
     counter results valid while any change to the code invalidates them."""
     code = []
-    for line in open(KERNEL_SRC, encoding="utf-8"):
-        line = line.split("//", 1)[0].rstrip()
-        if line:
-            code.append(line)
+    for path in KERNEL_SRCS:
+        for line in open(path, encoding="utf-8"):
+            line = line.split("//", 1)[0].rstrip()
+            if line:
+                code.append(line)
     return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 

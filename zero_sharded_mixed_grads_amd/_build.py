@@ -32,7 +32,7 @@ DEVICE = [f"--offload-arch={ARCH}", "-mcode-object-version=5", "-Xclang", "-targ
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HOST = [f"-I{ROCM}/include", "-D__HIP_PLATFORM_AMD__=1"]  # HIP runtime API from host C++
 
-SOURCES = ["zero_host.cpp", "zero_ckpt.cpp", "zero_offload.cpp", "zero_kernels.hip"]
+SOURCES = ["zero_host.cpp", "zero_ckpt.cpp", "zero_offload.cpp", "zero_kernels.hip", "zero_adam.hip"]
 # the host AdamW of the offload path: OpenMP threads, vectorisable sqrt, and the
 # exact operation sequence of the device kernel (no contraction)
 EXTRA = {"zero_offload.cpp": ["-fopenmp", "-fno-math-errno", "-ffp-contract=off"]}
