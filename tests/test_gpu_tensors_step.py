@@ -142,9 +142,9 @@ def test_tensor_step_rejects_split_fp32_phases_and_overlap():
         z.zero_adam_step_tensors(z.adamw(), ts, numels, "f16", 0, 300, th, m, v, p, "f16", None,
                                  st)
     assert e.value.status == z.ZERO_EALIGN
-    with pytest.raises(z.ZeroError) as e:  # param_out inside the gradient tensor it reads
+    with pytest.raises(z.ZeroError) as e:  # param_out over gradients the step reads
         z.zero_adam_step_tensors(z.adamw(), ts, numels, "f16", 0, 300, th, m, buf[1200:1500],
-                                 ts[0][500:800], "f16", None, st)
+                                 ts[0][100:400], "f16", None, st)
     assert e.value.status == z.ZERO_EINVAL and "param_out overlaps tensor 0" in str(e.value)
     assert z.read_adam_state(st).step == 0  # nothing ran
 

@@ -159,9 +159,33 @@ __global__ void __launch_bounds__(kBlock) flatten_segments(FlatArgs a)
 // kStatsTilesPerBlock consecutive tiles and, for each, sums exactly the
 // squares that flatten_segments<2, stats> sums for it, in the same order
 // (the tile's edge elements first, then its thread's line), and leaves the
-// same per-tile partial.  The loads of all its tiles are issued before any is
-// summed, so a block keeps several lines per thread in flight.
+// same per-tile partial.  Consecutive tiles mostly lie in one segment, so the
+// table is searched again only when a tile starts a new one; the loads of all
+// the block's tiles are issued before any is summed, and the per-tile sums
+// share one pass over LDS.
 constexpr int kStatsTilesPerBlock = 4;
+
+// Per-tile block sums of x[0..T) in a fixed order (within each wave by DPP,
+// then the wave totals in wave order, as block_sum does); thread q < T ends
+// with the sum of x[q].
+template <int T>
+__device__ __forceinline__ double block_sums(double (&x)[T])
+{
+    __shared__ double s_part[T][kBlock / 64];
+#pragma unroll
+    for (int q = 0; q < T; ++q)
+        x[q] = wave_sum(x[q]);
+    if (threadIdx.x % 64 == 0)
+#pragma unroll
+        for (int q = 0; q < T; ++q)
+            s_part[q][threadIdx.x / 64] = x[q];
+    __syncthreads();
+    double t = 0.0;
+    if (threadIdx.x < T)
+        for (int i = 0; i < kBlock / 64; ++i)
+            t += s_part[threadIdx.x][i];
+    return t;
+}
 
 template <bool BF16>
 __global__ void __launch_bounds__(kBlock) stats_segments(FlatArgs a)
@@ -172,16 +196,19 @@ __global__ void __launch_bounds__(kBlock) stats_segments(FlatArgs a)
     bool line[T];
     uint16_t edge[T];
     bool has_edge[T];
+    const uint32_t tile0 = blockIdx.x * T;
+    uint32_t s = find_segment(a, tile0);
     // the lines of every tile first, then the edge elements, then the sums
 #pragma unroll
     for (int q = 0; q < T; ++q) {
         line[q] = has_edge[q] = false;
         sb[q] = 0;
         hi[q] = make_uint4(0, 0, 0, 0);
-        const uint32_t tile = blockIdx.x * T + q;
+        const uint32_t tile = tile0 + q;
         if (tile >= a.n_tiles)
             continue;
-        const uint32_t s = find_segment(a, tile);
+        if (tile >= a.tile_lo[s + 1])  // the tile starts a later segment
+            s = find_segment(a, tile);
         const uint64_t e_lo = a.seg_lo[s], e_hi = a.seg_lo[s + 1];
         const uint64_t ph = a.dst_phase;
         const uint64_t c0 = (e_lo + ph + 7) / 8, c1 = (e_hi + ph) / 8;
@@ -212,27 +239,25 @@ __global__ void __launch_bounds__(kBlock) stats_segments(FlatArgs a)
             }
         }
     }
+    double acc[T];
 #pragma unroll
     for (int q = 0; q < T; ++q) {
-        double acc = 0.0;
+        acc[q] = 0.0;
         if (has_edge[q]) {
             const double x = (double)to_f32<BF16>(edge[q]);
-            acc = fma(x, x, acc);
+            acc[q] = fma(x, x, acc[q]);
         }
         if (line[q]) {
             const uint4 o = sb[q] ? shift_lines_rt(lo[q], hi[q], sb[q]) : lo[q];
-            accum2<BF16>(o.x, acc);
-            accum2<BF16>(o.y, acc);
-            accum2<BF16>(o.z, acc);
-            accum2<BF16>(o.w, acc);
-        }
-        const uint32_t tile = blockIdx.x * T + q;
-        if (tile < a.n_tiles) {  // uniform: every thread of the block takes the barrier
-            const double t = block_sum(acc);
-            if (threadIdx.x == 0)
-                a.part[a.tile_base + tile] = t;
+            accum2<BF16>(o.x, acc[q]);
+            accum2<BF16>(o.y, acc[q]);
+            accum2<BF16>(o.z, acc[q]);
+            accum2<BF16>(o.w, acc[q]);
         }
     }
+    const double t = block_sums<T>(acc);
+    if (threadIdx.x < T && tile0 + threadIdx.x < a.n_tiles)
+        a.part[a.tile_base + tile0 + threadIdx.x] = t;
 }
 
 // ============================================================ grad stats
