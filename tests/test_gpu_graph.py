@@ -1,7 +1,10 @@
 """One whole step captured in a HIP graph: the fused gather+stats, AdamW and
 the loss-scale update record only kernels (no memset, allocation or
 synchronisation), so replaying the graph must give, replay after replay,
-bit for bit what the same calls give eagerly."""
+bit for bit what the same calls give eagerly.  The same for the step read in
+place from the per-tensor gradients, and for the step whose statistics use
+the library's own scratch (zero_grad_stats_noalloc, meant for callers under
+graph capture)."""
 import numpy as np
 import pytest
 import torch
@@ -31,12 +34,24 @@ class _Rank:
         self.ws = torch.empty(nb, dtype=torch.uint8, device=dev())
         self.hp = z.adamw(max_grad_norm=1.0, inv_loss_scale=float("nan"))  # scale from device
 
-    def step(self):
-        z.zero_bucket_flatten_stats(self.grads, self.numels, "f16", 0, self.n, self.g,
-                                    float("nan"), self.ws, self.ws.numel(), self.stats,
-                                    d_scale=self.scale)
-        z.zero_adam_step(self.hp, self.g, "f16", self.th, self.m, self.v, self.p, "f16", self.n,
-                         self.stats, self.state, d_scale=self.scale)
+    def step(self, kind="gathered"):
+        if kind == "tensors":  # read in place: no gathered shard
+            z.zero_grad_stats_tensors(self.grads, self.numels, "f16", 0, self.n, float("nan"),
+                                      self.ws, self.ws.numel(), self.stats, d_scale=self.scale)
+            z.zero_adam_step_tensors(self.hp, self.grads, self.numels, "f16", 0, self.n, self.th,
+                                     self.m, self.v, self.p, "f16", self.stats, self.state,
+                                     d_scale=self.scale)
+        else:
+            if kind == "noalloc":  # gather, then statistics in the library's scratch
+                z.zero_bucket_flatten(self.grads, self.numels, "f16", 0, self.n, self.g)
+                z.zero_grad_stats_noalloc(self.g, "f16", self.n, float("nan"), self.stats,
+                                          d_scale=self.scale)
+            else:
+                z.zero_bucket_flatten_stats(self.grads, self.numels, "f16", 0, self.n, self.g,
+                                            float("nan"), self.ws, self.ws.numel(), self.stats,
+                                            d_scale=self.scale)
+            z.zero_adam_step(self.hp, self.g, "f16", self.th, self.m, self.v, self.p, "f16",
+                             self.n, self.stats, self.state, d_scale=self.scale)
         z.zero_loss_scale_update(self.cfg, self.stats, self.scale)
 
     def snapshot(self):
@@ -44,7 +59,8 @@ class _Rank:
                 (self.g, self.th, self.m, self.v, self.p, self.stats, self.state, self.scale)]
 
 
-def test_step_replays_in_a_graph_bit_for_bit():
+@pytest.mark.parametrize("kind", ["gathered", "tensors", "noalloc"])
+def test_step_replays_in_a_graph_bit_for_bit(kind):
     numels = [70_001, 13, 30_003]
     n = sum(numels)
     rng = np.random.default_rng(11)
@@ -66,12 +82,12 @@ def test_step_replays_in_a_graph_bit_for_bit():
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         warm = _Rank(numels, th0, cfg)
-        warm.step()
+        warm.step(kind)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        graphed.step()
+        graphed.step(kind)
     torch.cuda.synchronize()
     assert z.read_adam_state(graphed.state).step == 0  # capture ran nothing
 
@@ -79,7 +95,7 @@ def test_step_replays_in_a_graph_bit_for_bit():
         load_grads(k)
         torch.cuda.synchronize()
         graph.replay()
-        eager.step()
+        eager.step(kind)
         torch.cuda.synchronize()
         a, b = eager.snapshot(), graphed.snapshot()
         names = ["g", "master", "m", "v", "param", "stats", "state", "scale"]

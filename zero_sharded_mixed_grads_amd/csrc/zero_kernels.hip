@@ -163,7 +163,10 @@ __global__ void __launch_bounds__(kBlock) flatten_segments(FlatArgs a)
 // table is searched again only when a tile starts a new one; the loads of all
 // the block's tiles are issued before any is summed, and the per-tile sums
 // share one pass over LDS.
-constexpr int kStatsTilesPerBlock = 4;
+#ifndef ZERO_STATS_TILES
+#define ZERO_STATS_TILES 4
+#endif
+constexpr int kStatsTilesPerBlock = ZERO_STATS_TILES;
 
 // Per-tile block sums of x[0..T) in a fixed order (within each wave by DPP,
 // then the wave totals in wave order, as block_sum does); thread q < T ends
