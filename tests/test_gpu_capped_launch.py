@@ -164,3 +164,40 @@ def test_gather_launch_pieces_equal_default_build(stats):
         assert outs[0][1].sq_norm == outs[1][1].sq_norm and outs[1][1].overflow == 0
         sq, _ = oracle.grad_stats(outs[1][0], "f16", 1.0)
         assert abs(outs[1][1].sq_norm - sq) <= 1e-12 * sq
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("p_phase", [0, 3])
+@pytest.mark.parametrize("f_phase", [0, 1])
+def test_tensor_step_launch_pieces_equal_default_build(p_phase, f_phase):
+    """The step read in place from five tensors (one of 1,000,000 elements, 489
+    tiles) over a dozen launches of at most 64 tiles, the large tensor split
+    between launches: statistics and every output equal the default build's bit
+    for bit."""
+    numels = [300_001, 7, 1_000_000, 33, 200_000]
+    lo, hi = 5, sum(numels) - 3
+    n = hi - lo
+    host = [gen.f32_to_bits16((np.random.default_rng(10 + i).standard_normal(k) * 1e-3 * 1024)
+                              .astype(np.float32), "f16") for i, k in enumerate(numels)]
+    ts = [torch.from_numpy(h.view(np.int16)).to(dev()) for h in host]
+    hp = AdamW(max_grad_norm=0.5, inv_loss_scale=1.0 / 1024)
+    outs = []
+    for ctx in (contextlib.nullcontext(), capped()):
+        with ctx:
+            c = _state(n, 0, p_phase, f_phase, 99)
+            gs, st = z.new_grad_stats(dev()), z.new_adam_state(dev())
+            nb = z.zero_bucket_flatten_stats_workspace(numels, lo, n)
+            ws = torch.empty(nb, dtype=torch.uint8, device=dev())
+            for _ in range(2):
+                z.zero_grad_stats_tensors(ts, numels, "f16", lo, n, hp.inv_loss_scale, ws, nb, gs)
+                z.zero_adam_step_tensors(z.adamw(**hp.__dict__), ts, numels, "f16", lo, n,
+                                         c["th"].ptr(), c["m"].ptr(), c["v"].ptr(), c["p"].ptr(),
+                                         "f16", gs, st)
+            torch.cuda.synchronize()
+            for k in ("th", "m", "v", "p"):
+                assert c[k].canaries_intact(), k
+            outs.append((z.read_grad_stats(gs), _raw(c), bytes(st.cpu().numpy())))
+    (sa, ra, ta), (sb, rb, tb) = outs
+    assert sa.sq_norm == sb.sq_norm and sa.overflow == sb.overflow == 0 and ta == tb
+    for k in ra:
+        assert np.array_equal(ra[k].view(np.uint8), rb[k].view(np.uint8)), k

@@ -149,6 +149,45 @@ def test_tensor_step_rejects_split_fp32_phases_and_overlap():
     assert z.read_adam_state(st).step == 0  # nothing ran
 
 
+@pytest.mark.parametrize("case", ["empty_tensors", "short", "empty_range", "one_tensor_middle"])
+def test_tensor_step_edge_ranges(case):
+    """Zero-size tensors in the list, ranges shorter than a chunk, an empty
+    range (the step counter still advances), and a range inside one tensor:
+    equal to the step on the gathered shard, bit for bit."""
+    numels = {"empty_tensors": [0, 1000, 0, 0, 37, 0, 5000],
+              "short": [3, 2, 4, 1],
+              "empty_range": [100, 200],
+              "one_tensor_middle": [50, 100_000, 70]}[case]
+    lo, hi = {"empty_tensors": (1, 6036), "short": (1, 7), "empty_range": (150, 150),
+              "one_tensor_middle": (1001, 60_003)}[case]
+    n = hi - lo
+    hp = AdamW(max_grad_norm=0.5, inv_loss_scale=1.0 / 1024)
+    ahp = z.adamw(**hp.__dict__)
+    host = _host_list(numels, "bf16", 5, 1024.0)
+    ts = [torch.from_numpy(h.view(np.int16)).to(dev()) if h.size else None for h in host]
+    a_raw, (a_th, a_m, a_v), a_praw, a_p = _state(max(n, 1), 1, 5, 7, "bf16")
+    b_raw, (b_th, b_m, b_v), b_praw, b_p = _state(max(n, 1), 1, 5, 7, "bf16")
+    a_st, b_st = z.new_adam_state(dev()), z.new_adam_state(dev())
+    a_gs, b_gs = z.new_grad_stats(dev()), z.new_grad_stats(dev())
+    nb = z.zero_bucket_flatten_stats_workspace(numels, lo, n)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev())
+    g = torch.empty(max(n, 1), dtype=torch.int16, device=dev())
+    z.zero_grad_stats_tensors(ts, numels, "bf16", lo, n, hp.inv_loss_scale, ws, nb, a_gs)
+    z.zero_adam_step_tensors(ahp, ts, numels, "bf16", lo, n, a_th, a_m, a_v, a_p, "bf16", a_gs,
+                             a_st)
+    z.zero_bucket_flatten_stats(ts, numels, "bf16", lo, n, g, hp.inv_loss_scale, ws, nb, b_gs)
+    z.zero_adam_step(ahp, g, "bf16", b_th, b_m, b_v, b_p, "bf16", n, b_gs, b_st)
+    torch.cuda.synchronize()
+    sa, sb = z.read_grad_stats(a_gs), z.read_grad_stats(b_gs)
+    assert sa.overflow == sb.overflow == 0 and sa.sq_norm == sb.sq_norm
+    if n == 0:
+        assert sa.sq_norm == 0.0
+    for x, y in zip(a_raw + [a_praw], b_raw + [b_praw]):
+        assert torch.equal(x.view(torch.int32 if x.dtype == torch.float32 else torch.int16),
+                           y.view(torch.int32 if y.dtype == torch.float32 else torch.int16))
+    assert torch.equal(a_st, b_st) and z.read_adam_state(a_st).step == 1
+
+
 # --------------------------------------------------- workloads vs the oracle
 def _step_both(rt, rg, grads):
     rt.tensors_step(grads)
