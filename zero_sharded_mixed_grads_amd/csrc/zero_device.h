@@ -31,9 +31,9 @@ using zero::fail;
 #endif
 constexpr int kBlock = ZERO_BLOCK;  // threads per block (waves of 64 lanes)
 
-// Lines per thread of a gather tile (compile-time; the measured best).
+// 16-byte lines per thread in a gather tile (compile-time; the measured best).
 #ifndef ZERO_FLAT_CPT
-#define ZERO_FLAT_CPT 1      // 16-byte lines per thread in a flatten tile
+#define ZERO_FLAT_CPT 1
 #endif
 
 // Plain global accesses of the streaming kernels (non-temporal hints were
