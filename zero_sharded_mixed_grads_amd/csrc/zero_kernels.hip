@@ -49,6 +49,22 @@ __device__ __forceinline__ double block_sum(double x)
     return t;
 }
 
+// Segment s's entries of the gather's table.  A block reads them right after
+// the search, before any branch, so that they arrive in one round of scalar
+// loads: the search and this read are then the only dependent loads before
+// the block's first vector load (reading each entry where it is used cost
+// three more rounds, and the in-place statistics pass 6% on the 13B list).
+struct SegEntry {
+    uint64_t e_lo, e_hi;  // destination elements [e_lo, e_hi)
+    uint32_t t_lo, t_hi;  // the segment's tiles [t_lo, t_hi)
+    const char *src;      // source address of element e_lo
+};
+
+__device__ __forceinline__ SegEntry seg_entry(const FlatArgs &a, uint32_t s)
+{
+    return SegEntry{a.seg_lo[s], a.seg_lo[s + 1], a.tile_lo[s], a.tile_lo[s + 1], a.src[s]};
+}
+
 template <int ES, int SB, int MODE>
 __device__ __forceinline__ void flatten_full_chunks(const char *src_line0, char *dst_line0,
                                                     uint64_t c_beg, uint64_t c_end, double &acc)
@@ -92,14 +108,15 @@ __global__ void __launch_bounds__(kBlock) flatten_segments(FlatArgs a)
 {
     constexpr uint64_t V = 16 / ES;  // elements per 16-byte line
     const uint32_t tile = blockIdx.x;  // one tile per block: the grid is the tile count
-    const uint32_t s = find_segment(a, tile);
-    const uint64_t e_lo = a.seg_lo[s], e_hi = a.seg_lo[s + 1];
     const uint64_t ph = a.dst_phase;
+    char *const dst = a.dst;
+    const SegEntry g = seg_entry(a, find_segment(a, tile));
+    const uint64_t e_lo = g.e_lo, e_hi = g.e_hi;
     // full destination lines inside the segment: [c0, c1) in line units
     const uint64_t c0 = (e_lo + ph + V - 1) / V, c1 = (e_hi + ph) / V;
     const bool has_full = c1 > c0;
-    const uint64_t k = tile - a.tile_lo[s];  // tile within the segment
-    const char *src = a.src[s];
+    const uint64_t k = tile - g.t_lo;  // tile within the segment
+    const char *src = g.src;
     double acc = 0.0;
     if (k == 0) {
         // partial lines at both ends, element by element
@@ -111,13 +128,13 @@ __global__ void __launch_bounds__(kBlock) flatten_segments(FlatArgs a)
             const uint64_t e = i < n_head ? e_lo + i : tail_beg + (i - n_head);
             if constexpr (ES == 2) {
                 const uint16_t v = ld_global(reinterpret_cast<const uint16_t *>(src) + (e - e_lo));
-                reinterpret_cast<uint16_t *>(a.dst)[e] = v;
+                reinterpret_cast<uint16_t *>(dst)[e] = v;
                 if constexpr (MODE != kCopy) {
                     const double x = (double)to_f32<MODE == kStatsBF16>(v);
                     acc = fma(x, x, acc);
                 }
             } else {
-                reinterpret_cast<uint32_t *>(a.dst)[e] =
+                reinterpret_cast<uint32_t *>(dst)[e] =
                     ld_global(reinterpret_cast<const uint32_t *>(src) + (e - e_lo));
             }
         }
@@ -130,7 +147,7 @@ __global__ void __launch_bounds__(kBlock) flatten_segments(FlatArgs a)
         const uintptr_t s0 = (uintptr_t)(src + (c0 * V - ph - e_lo) * ES);
         const uint32_t sb = (uint32_t)(s0 & 15u);
         const char *sl = (const char *)(s0 - sb);
-        char *dl = a.dst + (c0 * V - ph) * ES;
+        char *dl = dst + (c0 * V - ph) * ES;
         switch (sb) {
         case 0: flatten_full_chunks<ES, 0, MODE>(sl, dl, t_beg, t_end, acc); break;
         case 4: flatten_full_chunks<ES, 4, MODE>(sl, dl, t_beg, t_end, acc); break;
@@ -200,7 +217,9 @@ __global__ void __launch_bounds__(kBlock) stats_segments(FlatArgs a)
     uint16_t edge[T];
     bool has_edge[T];
     const uint32_t tile0 = blockIdx.x * T;
-    uint32_t s = find_segment(a, tile0);
+    const uint64_t ph = a.dst_phase;
+    const uint32_t n_tiles = a.n_tiles;
+    SegEntry g = seg_entry(a, find_segment(a, tile0));
     // the lines of every tile first, then the edge elements, then the sums
 #pragma unroll
     for (int q = 0; q < T; ++q) {
@@ -208,16 +227,15 @@ __global__ void __launch_bounds__(kBlock) stats_segments(FlatArgs a)
         sb[q] = 0;
         hi[q] = make_uint4(0, 0, 0, 0);
         const uint32_t tile = tile0 + q;
-        if (tile >= a.n_tiles)
+        if (tile >= n_tiles)
             continue;
-        if (tile >= a.tile_lo[s + 1])  // the tile starts a later segment
-            s = find_segment(a, tile);
-        const uint64_t e_lo = a.seg_lo[s], e_hi = a.seg_lo[s + 1];
-        const uint64_t ph = a.dst_phase;
+        if (q > 0 && tile >= g.t_hi)  // the tile starts a later segment
+            g = seg_entry(a, find_segment(a, tile));
+        const uint64_t e_lo = g.e_lo, e_hi = g.e_hi;
         const uint64_t c0 = (e_lo + ph + 7) / 8, c1 = (e_hi + ph) / 8;
         const bool has_full = c1 > c0;
-        const uint64_t k = tile - a.tile_lo[s];
-        const uint16_t *src = reinterpret_cast<const uint16_t *>(a.src[s]);
+        const uint64_t k = tile - g.t_lo;
+        const uint16_t *src = reinterpret_cast<const uint16_t *>(g.src);
         if (has_full) {
             const uint64_t c = k * kFlatTileChunks + threadIdx.x;
             if (c < c1 - c0) {
@@ -259,7 +277,7 @@ __global__ void __launch_bounds__(kBlock) stats_segments(FlatArgs a)
         }
     }
     const double t = block_sums<T>(acc);
-    if (threadIdx.x < T && tile0 + threadIdx.x < a.n_tiles)
+    if (threadIdx.x < T && tile0 + threadIdx.x < n_tiles)
         a.part[a.tile_base + tile0 + threadIdx.x] = t;
 }
 
