@@ -429,19 +429,67 @@ def copy_probe(steps: int):
     print(json.dumps({"copy_probe": res}), flush=True)
 
 
-def configs_sweep(steps: int, warmup: int, spread: bool = True):
+def time_calls(fn, nbytes: int, steps: int, warmup: int) -> dict:
+    """Median and minimum of `steps` HIP-event-timed calls of fn after `warmup`
+    untimed ones, with the bandwidth that moving nbytes per call gives."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(steps):
+        a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        c.record()
+        evs.append((a, c))
+    torch.cuda.synchronize()
+    ms = sorted(x.elapsed_time(y) for x, y in evs)
+    med = ms[len(ms) // 2]
+    return {"ms_median": med, "ms_min": ms[0], "GB/s": nbytes / med / 1e6,
+            "frac": nbytes / med / 1e6 / HBM_PEAK_GBS}
+
+
+def time_calls_alternating(fns: dict, nbytes: int, steps: int, warmup: int) -> dict:
+    """time_calls for several calls at once, alternating them call by call
+    (a, b, a, b, ...) so that each sees the same state of the part."""
+    import torch
+    for _ in range(warmup):
+        for fn in fns.values():
+            fn()
+    torch.cuda.synchronize()
+    evs = {k: [] for k in fns}
+    for _ in range(steps):
+        for k, fn in fns.items():
+            a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            c.record()
+            evs[k].append((a, c))
+    torch.cuda.synchronize()
+    out = {}
+    for k, pairs in evs.items():
+        ms = sorted(x.elapsed_time(y) for x, y in pairs)
+        med = ms[len(ms) // 2]
+        out[k] = {"ms_median": med, "ms_min": ms[0], "GB/s": nbytes / med / 1e6,
+                  "frac": nbytes / med / 1e6 / HBM_PEAK_GBS}
+    return out
+
+
+def configs_sweep(steps: int, warmup: int, spread: bool = True, which=(2, 3, 4, 5)):
     """zero_grad_stats and zero_adam_step timed alone on the flat shard of each
     workload of at least 100M parameters (1.5B at Nd 1, 7.5B rank 3 of 8, 13B
     at Nd 1, 100B rank 399 of 400), with the 16-bit arrays at the element
-    phase the shard has in the flat layout; then a skipped (overflowing) step,
-    and the fused gather + statistics of the shard from its per-tensor
-    gradients.  Prints one JSON line."""
+    phase the shard has in the flat layout (for a shard off phase 0, AdamW
+    again on the same arrays with the 16-bit views at phase 0); then a skipped
+    (overflowing) step, and the fused gather + statistics of the shard from
+    its per-tensor gradients.  Prints one JSON line."""
     import torch
     import zero_sharded_mixed_grads_amd as z
     from synth import WORKLOADS, gen
     dev = torch.device("cuda:0")
     out = {}
-    for idx in (2, 3, 4, 5):
+    for idx in which:
         cfg = WORKLOADS[idx]
         b, e = z.zero_partition(cfg.psi, cfg.nd, cfg.rank)
         n, ph = e - b, b % 8
@@ -449,7 +497,8 @@ def configs_sweep(steps: int, warmup: int, spread: bool = True):
         gbuf, master, m, v, pbuf, layout = state_arrays(n + 8, tdt, dev, spread)
         g, p = gbuf[ph:ph + n], pbuf[ph:ph + n]
         master, m, v = master[:n], m[:n], v[:n]
-        gen.device_fill_normal_(g, cfg.grad_seed(0), cfg.grad_sigma, cfg.loss_scale)
+        # every element of gbuf finite: its phase-0 view is timed too
+        gen.device_fill_normal_(gbuf, cfg.grad_seed(0), cfg.grad_sigma, cfg.loss_scale)
         gen.device_fill_normal_(master, cfg.master_seed(), cfg.master_sigma)
         m.zero_()
         v.zero_()
@@ -463,25 +512,25 @@ def configs_sweep(steps: int, warmup: int, spread: bool = True):
                                                   n, stats, state),
         }
         res = {"n": n, "dtype": cfg.dtype, "phase16": ph, "state_layout": layout}
-        for name, fn in calls.items():
-            for _ in range(warmup):
-                fn()
-            torch.cuda.synchronize()
-            evs = []
-            for _ in range(steps):
-                a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                fn()
-                c.record()
-                evs.append((a, c))
-            torch.cuda.synchronize()
-            ms = sorted(x.elapsed_time(y) for x, y in evs)
-            bpp = ADAM_BYTES_PER_PARAM if name == "adam_step" else STATS_BYTES_PER_PARAM
-            med = ms[len(ms) // 2]
-            res[name] = {"ms_median": med, "ms_min": ms[0], "GB/s": bpp * n / med / 1e6,
-                         "frac": bpp * n / med / 1e6 / HBM_PEAK_GBS}
+        res["grad_stats"] = time_calls(calls["grad_stats"], STATS_BYTES_PER_PARAM * n, steps,
+                                       warmup)
+        if ph:
+            # the same arrays with the 16-bit views moved to phase 0, timed call
+            # by call in turn with the shard's own phase: what the realigning
+            # variant costs on these buffers
+            g0, p0 = gbuf[:n], pbuf[:n]
+            res.update(time_calls_alternating(
+                {"adam_step": calls["adam_step"],
+                 "adam_step_phase0": lambda: z.zero_adam_step(hp, g0, cfg.dtype, master, m, v,
+                                                              p0, cfg.dtype, n, stats, state)},
+                ADAM_BYTES_PER_PARAM * n, steps, warmup))
+            del g0, p0
+        else:
+            res["adam_step"] = time_calls(calls["adam_step"], ADAM_BYTES_PER_PARAM * n, steps,
+                                          warmup)
         st = z.read_adam_state(state)
-        if st.skip or st.step != warmup + steps:
+        expect = (warmup + steps) * (2 if ph else 1)
+        if st.skip or st.step != expect:
             raise SystemExit(f"{cfg.name}: a step was skipped; timing would be invalid")
         # the skip path: one non-finite gradient, then AdamW writes nothing
         g[0] = float("inf")
@@ -496,7 +545,7 @@ def configs_sweep(steps: int, warmup: int, spread: bool = True):
         torch.cuda.synchronize()
         ms = sorted(x.elapsed_time(y) for x, y in ms)
         st = z.read_adam_state(state)
-        if not st.skip or st.step != warmup + steps:
+        if not st.skip or st.step != expect:
             raise SystemExit(f"{cfg.name}: the overflowing steps were not skipped")
         res["adam_step_skipped"] = {"ms_median": ms[len(ms) // 2], "ms_min": ms[0]}
         # the fused gather + statistics of the shard from its per-tensor gradients,
@@ -536,8 +585,10 @@ def configs_sweep(steps: int, warmup: int, spread: bool = True):
             del grads, ptrs, nums, fws
         out[cfg.name] = res
         gs = res["gather_stats"]
+        ph0 = (f"; at phase 0 {res['adam_step_phase0']['ms_median']:.3f} ms"
+               if ph else "")
         log(f"[bench] {cfg.name}: n={n} adam {res['adam_step']['ms_median']:.3f} ms "
-            f"({res['adam_step']['GB/s']:.0f} GB/s); gather+stats "
+            f"({res['adam_step']['GB/s']:.0f} GB/s{ph0}); gather+stats "
             + (f"{gs['ms_median']:.3f} ms ({gs['GB/s']:.0f} GB/s, {gs['tensors']} tensors)"
                if isinstance(gs, dict) else gs))
         del gbuf, pbuf, g, p, master, m, v, ws, calls
@@ -708,8 +759,9 @@ def main():
     ap.add_argument("--separate", action="store_true",
                     help="allocate the five state arrays separately instead of spreading "
                          "them over one pool")
-    ap.add_argument("--configs", action="store_true",
-                    help="time grad stats and AdamW alone on every workload of >= 100M params")
+    ap.add_argument("--configs", nargs="*", type=int, default=None,
+                    help="time grad stats and AdamW alone on every workload of >= 100M params "
+                         "(2 3 4 5), or on those listed")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one data-parallel rank's shard on one GPU; it does not "
@@ -726,8 +778,12 @@ def main():
     if args.ckpt:
         ckpt_bench()
         return
-    if args.configs:
-        configs_sweep(args.steps, args.warmup, spread=not args.separate)
+    if args.configs is not None:
+        bad = [i for i in args.configs if i not in (2, 3, 4, 5)]
+        if bad:
+            ap.error(f"--configs takes workloads 2 3 4 5, not {bad}")
+        configs_sweep(args.steps, args.warmup, spread=not args.separate,
+                      which=tuple(args.configs) or (2, 3, 4, 5))
         return
 
     import torch
