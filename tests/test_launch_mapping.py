@@ -1,7 +1,9 @@
 """Host-side model of AdamW's block -> chunk mapping (the one written in
 adamw_stream: tiles renumbered over the 8 XCDs, a capped grid looping over
 rounds of tiles), checked for tiny caps and sizes: every 8-element chunk of
-the body is updated exactly once, whatever the cap.  ZeRO-DP Stage 1 ("ZeRO:
+the body is updated exactly once, whatever the cap.  The same for the
+gather's and the statistics passes' renumbering of tiles (or groups of
+tiles) over a grid rounded up to a multiple of 8.  ZeRO-DP Stage 1 ("ZeRO:
 Memory Optimizations Toward Training Trillion Parameter Models", paper
 summary page): a rank updates all of its part, once."""
 import math
@@ -49,4 +51,45 @@ def test_uncapped_grid_is_one_round():
     grid = adam_grid(nchunks, 1 << 30)
     assert grid * BLOCK >= nchunks and (grid - 8) * BLOCK < nchunks
     count, _ = chunks_updated(nchunks, 1 << 30)
+    assert (count == 1).all()
+
+
+def xcd_tile(b, grid):
+    """The gather's and the statistics passes' block -> tile (or tile group)
+    renumbering: each XCD (block b runs on XCD b mod 8) takes a contiguous
+    eighth of a grid rounded up to a multiple of 8."""
+    return (b % 8) * (grid // 8) + b // 8
+
+
+@pytest.mark.parametrize("units", [1, 7, 8, 9, 63, 64, 65, 1000, 8_388_600])
+def test_xcd_renumbering_covers_each_unit_once(units):
+    """Blocks whose renumbered index is at or past the unit count exit; the
+    others cover [0, units) exactly once, and the eight XCDs' shares are
+    contiguous runs."""
+    grid = (units + 7) // 8 * 8
+    b = np.arange(grid)
+    t = (b % 8) * (grid // 8) + b // 8
+    assert sorted(t.tolist()) == list(range(grid))  # a permutation of the grid
+    live = t[t < units]
+    assert np.array_equal(np.sort(live), np.arange(units))
+    for x in range(8):
+        mine = np.sort(t[b % 8 == x])
+        assert (np.diff(mine) == 1).all()
+
+
+@pytest.mark.parametrize("T", [1, 2, 4])
+@pytest.mark.parametrize("n_tiles", [1, 3, 4, 5, 31, 32, 33, 64, 4097])
+def test_stats_groups_cover_each_tile_once(T, n_tiles):
+    """The in-place statistics pass: block b takes the T tiles from
+    xcd_tile(b) * T on, skipping tiles past the table; every tile once."""
+    groups = (n_tiles + T - 1) // T
+    grid = (groups + 7) // 8 * 8
+    count = np.zeros(n_tiles, np.int64)
+    for b in range(grid):
+        tile0 = xcd_tile(b, grid) * T
+        if tile0 >= n_tiles:
+            continue
+        for q in range(T):
+            if tile0 + q < n_tiles:
+                count[tile0 + q] += 1
     assert (count == 1).all()

@@ -65,6 +65,17 @@ __device__ __forceinline__ SegEntry seg_entry(const FlatArgs &a, uint32_t s)
     return SegEntry{a.seg_lo[s], a.seg_lo[s + 1], a.tile_lo[s], a.tile_lo[s + 1], a.src[s]};
 }
 
+// Tile of block b in a grid of `grid` blocks (a multiple of 8).  Block b runs
+// on XCD b mod 8, and each XCD has its own L2: renumbering the tiles as
+// (b mod 8) * grid/8 + b/8 gives every XCD a contiguous eighth of them, so
+// that a 64-byte sector shared by two neighbouring tiles (tiles are 16-byte
+// aligned, not 64-byte aligned, when the data sits at a 16-bit phase other
+// than 0) is fetched or written back by one L2 instead of two.
+__device__ __forceinline__ uint32_t xcd_tile(uint32_t b, uint32_t grid)
+{
+    return (b % 8) * (grid / 8) + b / 8;
+}
+
 template <int ES, int SB, int MODE>
 __device__ __forceinline__ void flatten_full_chunks(const char *src_line0, char *dst_line0,
                                                     uint64_t c_beg, uint64_t c_end, double &acc)
@@ -107,7 +118,9 @@ template <int ES, int MODE>
 __global__ void __launch_bounds__(kBlock) flatten_segments(FlatArgs a)
 {
     constexpr uint64_t V = 16 / ES;  // elements per 16-byte line
-    const uint32_t tile = blockIdx.x;  // one tile per block: the grid is the tile count
+    const uint32_t tile = xcd_tile(blockIdx.x, gridDim.x);  // one tile per block
+    if (tile >= a.n_tiles)  // the grid is the tile count rounded up to a multiple of 8
+        return;
     const uint64_t ph = a.dst_phase;
     char *const dst = a.dst;
     const SegEntry g = seg_entry(a, find_segment(a, tile));
@@ -216,9 +229,13 @@ __global__ void __launch_bounds__(kBlock) stats_segments(FlatArgs a)
     bool line[T];
     uint16_t edge[T];
     bool has_edge[T];
-    const uint32_t tile0 = blockIdx.x * T;
-    const uint64_t ph = a.dst_phase;
     const uint32_t n_tiles = a.n_tiles;
+    // groups of T tiles, renumbered per XCD; the grid is the group count
+    // rounded up to a multiple of 8
+    const uint32_t tile0 = xcd_tile(blockIdx.x, gridDim.x) * T;
+    if (tile0 >= n_tiles)
+        return;
+    const uint64_t ph = a.dst_phase;
     SegEntry g = seg_entry(a, find_segment(a, tile0));
     // the lines of every tile first, then the edge elements, then the sums
 #pragma unroll
@@ -347,33 +364,44 @@ __device__ __forceinline__ void stats_tile(const uint16_t *g, uint64_t head, uin
     }
 }
 
-// One tile per block: block b leaves the partial of tile tile0 + b.
+// One tile per block: the launch takes tiles [tile0, tile0 + tiles), block b
+// the tile tile0 + xcd_tile(b, grid) (the grid is `tiles` rounded up to a
+// multiple of 8), and leaves its partial.
 template <bool BF16>
 __global__ void __launch_bounds__(kBlock)
     stats_pass1(const uint16_t *g, uint64_t head, uint64_t nchunks, uint64_t tail_beg, uint64_t n,
-                uint64_t tile0, double *part)
+                uint64_t tile0, uint32_t tiles, double *part)
 {
+    const uint32_t k = xcd_tile(blockIdx.x, gridDim.x);
+    if (k >= tiles)
+        return;
     double acc = 0.0;
-    const uint64_t tile = tile0 + blockIdx.x;
+    const uint64_t tile = tile0 + k;
     stats_tile<BF16>(g, head, nchunks, tail_beg, n, tile, acc);
     const double t = block_sum(acc);
     if (threadIdx.x == 0)
         part[tile] = t;
 }
 
-// A fixed number of partials for any n: block b sums tiles b, b + gridDim.x,
-// b + 2 gridDim.x, ... and leaves one partial, part[b].
+// A fixed number of partials for any n: partial j (j < slots) sums tiles
+// j, j + slots, j + 2 slots, ... and is left in part[j].  The grid is slots
+// rounded up to a multiple of 8, and block b computes partial xcd_tile(b), so
+// that neighbouring tiles of one round are read through one XCD's L2; which
+// block computes a partial does not change its value.
 template <bool BF16>
 __global__ void __launch_bounds__(kBlock)
     stats_pass1_strided(const uint16_t *g, uint64_t head, uint64_t nchunks, uint64_t tail_beg,
-                        uint64_t n, uint64_t tiles, double *part)
+                        uint64_t n, uint64_t tiles, uint32_t slots, double *part)
 {
+    const uint32_t j = xcd_tile(blockIdx.x, gridDim.x);
+    if (j >= slots)
+        return;
     double acc = 0.0;
-    for (uint64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x)
+    for (uint64_t tile = j; tile < tiles; tile += slots)
         stats_tile<BF16>(g, head, nchunks, tail_beg, n, tile, acc);
     const double t = block_sum(acc);
     if (threadIdx.x == 0)
-        part[blockIdx.x] = t;
+        part[j] = t;
 }
 
 // Block b sums partials [b*kReduceGroup, (b+1)*kReduceGroup) in a fixed order.
@@ -449,8 +477,9 @@ __global__ void loss_scale_update(zero_loss_scaler c, const zero_grad_stats_t *s
 template <int ES, int MODE>
 zero_status flatten_launch(FlatArgs &a, hipStream_t stream)
 {
-    // one tile per block
-    hipLaunchKernelGGL((flatten_segments<ES, MODE>), dim3(a.n_tiles), dim3(kBlock), 0, stream, a);
+    // one tile per block, the grid rounded up to whole rounds of the 8 XCDs
+    hipLaunchKernelGGL((flatten_segments<ES, MODE>), dim3((a.n_tiles + 7) / 8 * 8), dim3(kBlock),
+                       0, stream, a);
     return launch_status("zero_bucket_flatten");
 }
 
@@ -629,16 +658,18 @@ extern "C" zero_status zero_grad_stats(const void *grad, zero_dtype gdt, uint64_
     const StatsLayout l = stats_layout(grad, n);
     double *part = (double *)workspace;
     const uint16_t *g = (const uint16_t *)grad;
-    // one tile per block, in launches of at most kMaxLaunchBlocks blocks
+    // one tile per block, in launches of at most kMaxLaunchBlocks tiles (a
+    // multiple of 8, so the rounded-up grid stays within it)
     for (uint64_t t0 = 0; t0 < l.tiles; t0 += kMaxLaunchBlocks) {
-        const uint32_t grid = (uint32_t)(l.tiles - t0 < kMaxLaunchBlocks ? l.tiles - t0
-                                                                         : kMaxLaunchBlocks);
+        const uint32_t tiles = (uint32_t)(l.tiles - t0 < kMaxLaunchBlocks ? l.tiles - t0
+                                                                          : kMaxLaunchBlocks);
+        const uint32_t grid = (tiles + 7) / 8 * 8;
         if (gdt == ZERO_BF16)
             hipLaunchKernelGGL(stats_pass1<true>, dim3(grid), dim3(kBlock), 0, s, g, l.head,
-                               l.nchunks, l.tail_beg, n, t0, part);
+                               l.nchunks, l.tail_beg, n, t0, tiles, part);
         else
             hipLaunchKernelGGL(stats_pass1<false>, dim3(grid), dim3(kBlock), 0, s, g, l.head,
-                               l.nchunks, l.tail_beg, n, t0, part);
+                               l.nchunks, l.tail_beg, n, t0, tiles, part);
         const zero_status st = launch_status("zero_grad_stats pass 1");
         if (st != ZERO_OK)
             return st;
@@ -653,7 +684,8 @@ extern "C" zero_status zero_grad_stats(const void *grad, zero_dtype gdt, uint64_
 // Host code reaches it only through the address that hipGetSymbolAddress
 // returns for the current device (the array's name is a host-side stand-in).
 constexpr uint64_t kScratchPartials = 8192;
-static_assert(kScratchPartials <= kFinalMax, "one block must finish the scratch partials");
+static_assert(kScratchPartials <= kFinalMax && kScratchPartials % 8 == 0,
+              "one block must finish the scratch partials, a whole number of XCD rounds");
 static __device__ __align__(256) double scratch[kScratchPartials];
 
 namespace {
@@ -703,12 +735,13 @@ extern "C" zero_status zero_grad_stats_noalloc(const void *grad, zero_dtype gdt,
         return fail(ZERO_EINVAL, "%s: a buffer overlaps the library's scratch", what);
     hipStream_t s = (hipStream_t)stream;
     const uint16_t *g = (const uint16_t *)grad;
+    const uint32_t grid = ((uint32_t)blocks + 7) / 8 * 8;  // kScratchPartials is a multiple of 8
     if (gdt == ZERO_BF16)
-        hipLaunchKernelGGL(stats_pass1_strided<true>, dim3((uint32_t)blocks), dim3(kBlock), 0, s,
-                           g, l.head, l.nchunks, l.tail_beg, n, l.tiles, part);
+        hipLaunchKernelGGL(stats_pass1_strided<true>, dim3(grid), dim3(kBlock), 0, s, g, l.head,
+                           l.nchunks, l.tail_beg, n, l.tiles, (uint32_t)blocks, part);
     else
-        hipLaunchKernelGGL(stats_pass1_strided<false>, dim3((uint32_t)blocks), dim3(kBlock), 0, s,
-                           g, l.head, l.nchunks, l.tail_beg, n, l.tiles, part);
+        hipLaunchKernelGGL(stats_pass1_strided<false>, dim3(grid), dim3(kBlock), 0, s, g, l.head,
+                           l.nchunks, l.tail_beg, n, l.tiles, (uint32_t)blocks, part);
     if (zero_status st = launch_status("zero_grad_stats_noalloc pass 1"); st != ZERO_OK)
         return st;
     return reduce_partials(part, blocks, inv_loss_scale, d_scale, d_stats, s);
@@ -817,7 +850,8 @@ extern "C" zero_status zero_grad_stats_tensors(const void *const *tensor_ptrs,
     FlatArgs a{};
     a.part = (double *)workspace;
     auto launch = [&](FlatArgs &t) -> zero_status {
-        const uint32_t grid = (t.n_tiles + kStatsTilesPerBlock - 1) / kStatsTilesPerBlock;
+        const uint32_t groups = (t.n_tiles + kStatsTilesPerBlock - 1) / kStatsTilesPerBlock;
+        const uint32_t grid = (groups + 7) / 8 * 8;  // whole rounds of the 8 XCDs
         if (gdt == ZERO_BF16)
             hipLaunchKernelGGL(stats_segments<true>, dim3(grid), dim3(kBlock), 0, s, t);
         else
