@@ -409,8 +409,9 @@ zero_status zero_offload_staging_bytes(uint64_t chunk_elems, size_t *bytes);
  * travel device -> host and the new 16-bit params host -> device in chunks
  * of staging_bytes / 8 elements through `staging`, caller-owned pinned host
  * memory (e.g. from hipHostMalloc), two slots deep so that transfers overlap
- * the host update.  The host loop performs the device kernel's fp32
- * operations in the same order.  Synchronous: returns after the params have
+ * the host update.  The host loop evaluates the update with the device
+ * kernel's fp64 operations in the same order, so its results equal the
+ * device's bit for bit.  Synchronous: returns after the params have
  * reached the device (or at once when the step is skipped).
  * Errors: as zero_adam_step; ZERO_ENOSPC if staging holds fewer than 4096
  * elements per slot. */
