@@ -226,9 +226,10 @@ zero_status zero_grad_stats(const void *grad, zero_dtype gdt, uint64_t n, double
  * scratch, so calls that overlap in time on one GPU (on different streams,
  * or from different threads without ordering) race and may return wrong
  * statistics.  The first call on a device looks the scratch up with
- * hipGetSymbolAddress (no allocation).  Errors: as zero_grad_stats
- * (ZERO_EINVAL, ZERO_EALIGN), and ZERO_EDEVICE when there is no current
- * device or the lookup fails. */
+ * hipGetSymbolAddress (no allocation).  `stream` must belong to the current
+ * device, whose scratch the call uses.  Errors: as zero_grad_stats
+ * (ZERO_EINVAL, ZERO_EALIGN); ZERO_EINVAL also for a stream of another device;
+ * ZERO_EDEVICE when there is no current device or the lookup fails. */
 zero_status zero_grad_stats_noalloc(const void *grad, zero_dtype gdt, uint64_t n,
                                     double inv_loss_scale, const zero_loss_scale_t *d_scale,
                                     zero_grad_stats_t *d_stats, void *stream);

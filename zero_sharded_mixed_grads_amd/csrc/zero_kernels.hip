@@ -692,7 +692,9 @@ static __device__ __align__(256) double scratch[kScratchPartials];
 
 namespace {
 // Device address of `scratch` on the current device, looked up once per device.
-zero_status scratch_address(const char *what, double **out)
+// The kernels run on `stream`'s device, so that must be the current one (whose
+// copy of the array the address names).
+zero_status scratch_address(const char *what, hipStream_t stream, double **out)
 {
     constexpr int kMaxDev = 64;
     static std::mutex mu;
@@ -701,6 +703,12 @@ zero_status scratch_address(const char *what, double **out)
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev)
         return fail(ZERO_EDEVICE, "%s: no current HIP device (or device index %d >= %d)", what,
                     dev, kMaxDev);
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess)
+        return fail(ZERO_EINVAL, "%s: not a valid stream", what);
+    if (sdev != dev)
+        return fail(ZERO_EINVAL, "%s: the stream belongs to device %d, but device %d is current",
+                    what, (int)sdev, dev);
     std::lock_guard<std::mutex> lock(mu);
     if (!addr[dev]) {
         void *p = nullptr;
@@ -725,7 +733,7 @@ extern "C" zero_status zero_grad_stats_noalloc(const void *grad, zero_dtype gdt,
         st != ZERO_OK)
         return st;
     double *part = nullptr;
-    if (zero_status st = scratch_address(what, &part); st != ZERO_OK)
+    if (zero_status st = scratch_address(what, (hipStream_t)stream, &part); st != ZERO_OK)
         return st;
     const StatsLayout l = stats_layout(grad, n);
     // every tile is folded into one of at most kScratchPartials block partials,
