@@ -6,6 +6,7 @@ import os
 import re
 
 import numpy as np
+import torch
 import pytest
 from hypothesis import given, settings, strategies as st
 
@@ -364,3 +365,17 @@ def test_tensor_table_marshals_once_and_checks_lengths():
         z.zero_bucket_flatten_stats_workspace([3, 5, 7], 0, 15)
     with pytest.raises(ValueError):
         z.tensor_table([0x1000, None], [3, 5, 7])
+
+
+def test_binding_refuses_host_tensors_for_device_arguments():
+    """A host tensor where the C call takes a device pointer (or a device
+    address where it takes host memory) is refused by the binding, before
+    the library could hand it to a kernel."""
+    g = torch.zeros(64, dtype=torch.int16)
+    with pytest.raises(ValueError, match="expected a device tensor"):
+        z.zero_grad_stats(g, "f16", 64, 1.0, FAKE, 4096, FAKE + 8192, 0)
+    with pytest.raises(ValueError, match="expected a device tensor"):
+        z.zero_bucket_flatten([g], [64], "f16", 0, 64, FAKE, 0)
+    assert z._ptr(g, host=True) == g.data_ptr()
+    with pytest.raises(ValueError, match="contiguous"):
+        z._ptr(torch.zeros(8, 8).t(), host=True)

@@ -144,10 +144,20 @@ def _check(status: int):
         raise ZeroError(status, lib().zero_last_error().decode())
 
 
-def _ptr(x) -> Optional[int]:
+def _ptr(x, host: bool = False) -> Optional[int]:
+    """The address of a buffer argument: None, an integer address (passed as
+    it is), or a contiguous tensor on the device (host=False) or in host
+    memory (host=True).  A tensor on the wrong side or with gaps is refused
+    here, since the library cannot tell and the kernels would read the wrong
+    memory."""
     if x is None:
         return None
     if isinstance(x, torch.Tensor):
+        if x.is_cuda == host:
+            want = "host" if host else "device"
+            raise ValueError(f"expected a {want} tensor, got one on {x.device}")
+        if not x.is_contiguous():
+            raise ValueError("tensor arguments must be contiguous")
         return x.data_ptr()
     return int(x)
 
@@ -331,10 +341,12 @@ def zero_offload_adam_step(hp: AdamW, grad, gdtype, master_host, exp_avg_host, e
     """master/exp_avg/exp_avg_sq: host tensors (or addresses); staging: pinned
     host memory; grad, param_out, d_stats, d_state: device."""
     _check(lib().zero_offload_adam_step(ctypes.byref(hp), _ptr(grad), _dtype(gdtype),
-                                        _ptr(master_host), _ptr(exp_avg_host),
-                                        _ptr(exp_avg_sq_host), _ptr(param_out), _dtype(pdtype),
-                                        n, _ptr(d_stats), _ptr(d_scale), _ptr(d_state),
-                                        _ptr(staging), staging_bytes, _stream(stream)))
+                                        _ptr(master_host, host=True),
+                                        _ptr(exp_avg_host, host=True),
+                                        _ptr(exp_avg_sq_host, host=True), _ptr(param_out),
+                                        _dtype(pdtype), n, _ptr(d_stats), _ptr(d_scale),
+                                        _ptr(d_state), _ptr(staging, host=True), staging_bytes,
+                                        _stream(stream)))
 
 
 # ---------------------------------------------------- sharded checkpoints
