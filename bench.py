@@ -743,8 +743,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=4,
-                    help="workload: 4 = 13B list at Nd 1 (default), 2 = GPT-2 1.5B list at Nd 1")
+    ap.add_argument("--config", type=int, default=4, choices=(1, 2, 3, 4, 5),
+                    help="workload: 4 = 13B list at Nd 1 (default), 2 = GPT-2 1.5B list at "
+                         "Nd 1, 3 = 7.5B rank 3 of 8, 5 = 100B rank 399 of 400, 1 = the tiny "
+                         "ragged list (rank 0 of 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time plain device copies of a known size instead")
