@@ -1,4 +1,4 @@
-// Host-side driver for the sanitizer test: exercises every host planner call of
+// Host program of the sanitizer test: exercises every host planner call of
 // libzero_mi355x (zero_host.cpp) and the oracle's C functions over small grids,
 // error paths included, in a build with AddressSanitizer and UBSan.  Exits
 // non-zero on the first wrong result; the sanitizers abort on any report.

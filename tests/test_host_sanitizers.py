@@ -1,5 +1,5 @@
 """The host planner and the oracle built with AddressSanitizer and UBSan
-(host compilers only) run a driver over small grids and error paths; any
+(host compilers only) run a host program over small grids and error paths; any
 sanitizer report or wrong result fails the test."""
 import os
 import shutil

@@ -1,7 +1,7 @@
 """zero_grad_stats_noalloc (statistics with the library's own device scratch,
 for callers that cannot allocate) against zero_grad_stats with a caller
 workspace: the overflow flag bit-exact and the squared norm within the
-spec 1e-5 (it differs only in the order of the fp64 sums), over two
+1e-5 relative bar for the norm (it differs only in the order of the fp64 sums), over two
 calls in a row whose second input is smaller, so that partials left in the
 shared scratch by the first call cannot leak into the second."""
 import numpy as np
