@@ -215,17 +215,28 @@ __device__ __forceinline__ void store_tail_rt(uint16_t *next_line, const uint32_
     }
 }
 
-// The 16 bytes of lane `lane + d` (d = +1 or -1 within the wave).
+// A dword moved one lane along the whole wave by DPP: wave_shl:1 (CTRL 0x130)
+// gives lane i the value of lane i + 1, wave_shr:1 (0x138) that of lane i - 1;
+// the lane with no source (the last, the first) gets 0.  On the VALU, unlike
+// a ds_bpermute shuffle, which goes through the LDS unit.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_wave_shift(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+
+// The 16 bytes of lane + 1 (down) or lane - 1 (up) within the wave.  Callers
+// use only values that come from active lanes.
 __device__ __forceinline__ uint4 shfl_line_down(const uint4 &x)
 {
-    return make_uint4(__shfl_down(x.x, 1, 64), __shfl_down(x.y, 1, 64), __shfl_down(x.z, 1, 64),
-                      __shfl_down(x.w, 1, 64));
+    return make_uint4(dpp_wave_shift<0x130>(x.x), dpp_wave_shift<0x130>(x.y),
+                      dpp_wave_shift<0x130>(x.z), dpp_wave_shift<0x130>(x.w));
 }
 
 __device__ __forceinline__ uint4 shfl_line_up(const uint4 &x)
 {
-    return make_uint4(__shfl_up(x.x, 1, 64), __shfl_up(x.y, 1, 64), __shfl_up(x.z, 1, 64),
-                      __shfl_up(x.w, 1, 64));
+    return make_uint4(dpp_wave_shift<0x138>(x.x), dpp_wave_shift<0x138>(x.y),
+                      dpp_wave_shift<0x138>(x.z), dpp_wave_shift<0x138>(x.w));
 }
 
 // x moved across lanes by one DPP pattern (both 32-bit halves).  Only the
